@@ -1,0 +1,124 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/wsx.h declares, and rejects bad arguments on the host before anything
+is enqueued (no HIP call is reached on these paths)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from weight_streaming_expert_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wsx.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libwsx.so not built")
+
+FAKE = 0x7F0000000000          # 256-byte aligned fake device address, never dereferenced on these paths
+MIS = FAKE + 8                 # misaligned
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "for", "while", "sizeof")))
+
+
+def test_header_functions_are_exported_and_declared():
+    lib = _lib.load()
+    names = header_functions()
+    assert "moe_route_topk" in names and "moe_decode_step" in names and len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.EXPORTS, n
+
+
+def test_build_info_names_the_target():
+    info = _lib.load().wsx_build_info().decode()
+    assert "gfx950" in info and "lm_head" in info and "moe_gateup" in info
+
+
+def test_status_strings():
+    lib = _lib.load()
+    for s in range(8):
+        assert lib.wsx_status_string(s)
+
+
+def route(x=FAKE, w=FAKE, dt=0, T=1, H=2560, E=512, k=8, ids=FAKE, tw=FAKE, el=FAKE, sw=FAKE, lo=None, ws=FAKE,
+          wsb=1 << 20):
+    return _lib.load().moe_route_topk(x, w, dt, T, H, E, k, ids, tw, el, sw, lo, ws, wsb, None)
+
+
+def test_route_argument_errors():
+    assert route(x=None) == 1
+    assert route(ids=None) == 1
+    assert route(dt=7) == 6
+    assert route(T=0) == 2
+    assert route(T=5) == 4
+    assert route(k=9) == 4
+    assert route(k=0) == 2
+    assert route(E=4, k=8) == 2
+    assert route(E=2048) == 4
+    assert route(H=100) == 2
+    assert route(x=MIS) == 3
+    assert route(ws=None) == 5
+    assert route(wsb=16) == 5
+    assert route(ws=FAKE + 16) == 3
+
+
+def experts(x=FAKE, c13=FAKE, s13=FAKE, c2=FAKE, s2=FAKE, sh=(None, None, None, None), el=FAKE, sw=FAKE, T=1,
+            H=2560, I=768, E=512, k=8, res=None, y=FAKE, h=None, ws=FAKE, wsb=1 << 24):
+    return _lib.load().moe_expert_gemv_mxfp4(x, c13, s13, c2, s2, *sh, el, sw, T, H, I, E, k, res, y, h, ws, wsb, None)
+
+
+def test_expert_argument_errors():
+    assert experts(c13=None) == 1
+    assert experts(el=None) == 1
+    assert experts(sh=(FAKE, None, None, None)) == 1
+    assert experts(h=FAKE, res=None) == 1
+    assert experts(I=100) == 2
+    assert experts(H=0) == 2
+    assert experts(T=9) == 4
+    assert experts(I=32 * 1000) == 4
+    assert experts(c2=MIS) == 3
+    assert experts(wsb=100) == 5
+    lib = _lib.load()
+    need = lib.wsx_moe_workspace_bytes(1, 2560, 768, 512, 8)
+    assert need >= 9 * 768 * 4 and experts(wsb=need - 1) == 5
+
+
+def test_head_argument_errors():
+    lib = _lib.load()
+    assert lib.lm_head_quantize_fp8(None, 10, 256, FAKE, FAKE, None) == 1
+    assert lib.lm_head_quantize_fp8(FAKE, 0, 256, FAKE, FAKE, None) == 2
+    assert lib.lm_head_quantize_fp8(FAKE, 10, 250, FAKE, FAKE, None) == 2
+    assert lib.lm_head_quantize_fp8(FAKE, 10, 32768, FAKE, FAKE, None) == 4
+    assert lib.lm_head_quantize_fp8(MIS, 10, 256, FAKE, FAKE, None) == 3
+    f = lib.lm_head_gemv_fp8_argmax
+    assert f(FAKE, None, 10, 256, FAKE, 1, None, FAKE, FAKE, 1 << 20, None) == 1
+    assert f(FAKE, FAKE, 10, 256, FAKE, 0, None, FAKE, FAKE, 1 << 20, None) == 2
+    assert f(FAKE, FAKE, 10, 256, FAKE, 5, None, FAKE, FAKE, 1 << 20, None) == 4
+    assert f(FAKE, FAKE, 10, 256, FAKE, 1, None, FAKE, FAKE, 10, None) == 5
+    assert f(FAKE, FAKE, 10, 256 * 100, FAKE, 1, None, FAKE, FAKE, 1 << 20, None) == 4
+    g = lib.lm_head_gemv_bf16_argmax
+    assert g(FAKE, 10, 256, None, 1, None, FAKE, FAKE, 1 << 20, None) == 1
+    assert g(FAKE, 10, 256, FAKE, 1, None, FAKE, FAKE + 4, 1 << 20, None) == 3
+
+
+def test_decode_step_argument_errors():
+    lib = _lib.load()
+    st = _lib.MoeStack(FAKE, 0, FAKE, FAKE, FAKE, FAKE, None, None, None, None, 2, 2560, 768, 512, 8)
+    f = lib.moe_decode_step
+    args = lambda **kw: [kw.get("h", FAKE), kw.get("T", 1), ctypes.byref(kw.get("st", st)), FAKE, FAKE,
+                         kw.get("V", 157184), FAKE, None, FAKE, None, None, None, None, kw.get("ws", FAKE),
+                         kw.get("wsb", 1 << 26), None]
+    assert f(*args(h=None)) == 1
+    assert f(*args(V=0)) == 2
+    assert f(*args(T=6)) == 4
+    assert f(*args(wsb=1000)) == 5
+    bad = _lib.MoeStack(FAKE, 0, FAKE, FAKE, FAKE, FAKE, None, None, None, None, 0, 2560, 768, 512, 8)
+    assert f(*args(st=bad)) == 2
+    need = lib.wsx_decode_step_workspace_bytes(1, 2560, 768, 512, 8, 157184)
+    assert need > lib.wsx_moe_workspace_bytes(1, 2560, 768, 512, 8)

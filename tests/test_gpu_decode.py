@@ -1,0 +1,97 @@
+"""GPU parity of the whole decode step (stacked MoE layers with the RMS norm
+between them, then the FP8 head), checked layer by layer with teacher forcing:
+each layer's oracle check consumes the GPU's own residual stream h_l and
+normalized input u_l, so no stage inherits another stage's rounding."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import compare as C
+from oracle import head as OH
+from oracle import moe as OM
+from weight_streaming_expert_amd import configs, inputs
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ops():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from weight_streaming_expert_amd import ops as _ops
+    return _ops
+
+
+def build_stack(ops, wl, L):
+    layers = [inputs.layer_weights(wl, l) for l in range(L)]
+    st = lambda key: P.to_dev(np.stack([lw[key] for lw in layers]))
+    r = np.stack([lw["router"] for lw in layers])
+    router = P.to_dev(r) if r.dtype == np.float32 else P.to_dev_bf16(r)
+    shared = tuple(P.to_dev(np.stack([lw["shared"][i] for lw in layers])) for i in range(4))
+    stack = ops.MoeStackTensors(router, st("w13c"), st("w13s"), st("w2c"), st("w2s"), shared=shared, k=wl.moe.k)
+    return layers, stack
+
+
+def check_step(wl, layers, out, head_q, head_s, h0):
+    m = wl.moe
+    ht, ut = P.bits(out["h_trace"]), P.bits(out["u_trace"])
+    ids, ws = P.np_(out["ids_trace"]), P.np_(out["w_trace"])
+    assert np.array_equal(ht[0], h0)
+    for l, lw in enumerate(layers):
+        P.check_norm(ht[l], ut[l])
+        P.check_routing(ut[l], P.router_values(lw["router"]), m.k, ids[l], ws[l])
+        get = lambda e, lw=lw: (lw["w13c"][e], lw["w13s"][e], lw["w2c"][e], lw["w2s"][e])
+        y_ref = P.moe_y_ref(ut[l], ids[l], ws[l], get, lw["shared"], m.I)
+        P.check_h_next(ht[l], y_ref, ht[l + 1])
+    L = len(layers)
+    P.check_norm(ht[L], ut[L])
+    assert np.array_equal(P.bits(out["h"]), ht[L])
+    return P.check_head(head_q, head_s, ut[L], P.np_(out["logits"]), P.np_(out["argmax"]))
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_tiny_stack_decode_step(ops, T):
+    wl = configs.TINY
+    L = 3
+    layers, stack = build_stack(ops, wl, L)
+    head_w = inputs.head_weights(wl, K=wl.moe.H)
+    head = ops.Fp8LmHead.quantize(P.to_dev_bf16(head_w))
+    qh, sh = P.np_(head.q), P.np_(head.s)
+    for step in range(3):
+        h0 = inputs.normal_bf16((wl.seed, inputs.T_X, step, T), (T, wl.moe.H), 1.0)
+        out = ops.moe_decode_step(P.to_dev_bf16(h0), stack, head, trace=True)
+        check_step(wl, layers, out, qh, sh, h0)
+        plain = ops.moe_decode_step(P.to_dev_bf16(h0), stack, head, trace=False)
+        assert torch.equal(plain["h"], out["h"]) and torch.equal(plain["argmax"], out["argmax"])
+        assert torch.equal(plain["logits"], out["logits"])
+
+
+@pytest.fixture(scope="module")
+def ling_stack(ops):
+    wl = configs.DECODE_STEP
+    L = 2
+    layers, stack = build_stack(ops, wl, L)
+    head_w = inputs.head_weights(configs.LM_HEAD)
+    head = ops.Fp8LmHead.quantize(P.to_dev_bf16(head_w))
+    torch.cuda.synchronize()
+    return wl, layers, stack, head, P.np_(head.q), P.np_(head.s)
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_ling_shape_stack_decode_step(ops, ling_stack, T):
+    wl, layers, stack, head, qh, sh = ling_stack
+    for step in range(2):
+        h0 = inputs.normal_bf16((wl.seed, inputs.T_X, step, T), (T, wl.moe.H), 1.0)
+        out = ops.moe_decode_step(P.to_dev_bf16(h0), stack, head, trace=True)
+        check_step(wl, layers, out, qh, sh, h0)
+
+
+def test_decode_step_is_deterministic(ops, ling_stack):
+    wl, layers, stack, head, qh, sh = ling_stack
+    h0 = P.to_dev_bf16(inputs.normal_bf16((3,), (1, wl.moe.H), 1.0))
+    a = ops.moe_decode_step(h0, stack, head)
+    for _ in range(10):
+        b = ops.moe_decode_step(h0, stack, head)
+        assert torch.equal(a["h"], b["h"]) and torch.equal(a["logits"], b["logits"])

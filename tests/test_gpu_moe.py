@@ -1,0 +1,209 @@
+"""GPU parity of one MoE layer: router + top-k + compact expert list, and the
+MXFP4 routed + shared SwiGLU experts with the bf16 residual, at the tiny shape
+(H=256, 16 experts top-2), at the Ling shape (H=2560, 512 experts top-8,
+I=768) for 1 token and for the 4-token verify pass, plus exact planted cases,
+ties, edge cases and determinism."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import compare as C
+from oracle import formats as F
+from oracle import moe as OM
+from weight_streaming_expert_amd import configs, inputs
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ops():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from weight_streaming_expert_amd import ops as _ops
+    return _ops
+
+
+def run_layer(ops, wl, dw, x_bits, res_bits):
+    x = P.to_dev_bf16(x_bits)
+    r = ops.moe_route_topk(x, dw["router"], wl.moe.k)
+    y, h = ops.moe_expert_gemv_mxfp4(x, dw["w13c"], dw["w13s"], dw["w2c"], dw["w2s"], r["expert_list"], r["slot_w"],
+                                     wl.moe.k, shared=dw["shared"], residual=P.to_dev_bf16(res_bits))
+    return {k: P.np_(v) for k, v in r.items()}, P.np_(y), P.bits(h)
+
+
+def check_layer(wl, lw, x_bits, res_bits, r, y, h):
+    m = wl.moe
+    ties = P.check_routing(x_bits, P.router_values(lw["router"]), m.k, r["topk_ids"], r["topk_w"],
+                           r["expert_list"], r["slot_w"], r["logits"])
+    get = lambda e: (lw["w13c"][e], lw["w13s"][e], lw["w2c"][e], lw["w2s"][e])
+    y_ref = P.moe_y_ref(x_bits, r["topk_ids"], r["topk_w"], get, lw["shared"], m.I)
+    ok, worst = C.fp_close(y, y_ref)
+    assert ok, f"y off by {worst:.3e} x RMS"
+    P.check_residual(res_bits, y, h)
+    return ties, worst
+
+
+# ----------------------------------------------------------------------------- tiny shape
+
+
+@pytest.fixture(scope="module")
+def tiny(ops):
+    wl = configs.TINY
+    lw = inputs.layer_weights(wl, 0)
+    return wl, lw, P.layer_to_dev(lw)
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
+def test_tiny_layer(ops, tiny, T):
+    wl, lw, dw = tiny
+    for step in range(4):
+        x = inputs.normal_bf16((wl.seed, inputs.T_X, step, T), (T, wl.moe.H), 1.0)
+        res = inputs.normal_bf16((wl.seed, 99, step, T), (T, wl.moe.H), 1.0)
+        r, y, h = run_layer(ops, wl, dw, x, res)
+        check_layer(wl, lw, x, res, r, y, h)
+
+
+def test_tiny_handmade_expert_list_and_no_shared(ops, tiny):
+    wl, lw, dw = tiny
+    m = wl.moe
+    T = 2
+    x = inputs.normal_bf16((3, 1), (T, m.H), 1.0)
+    ids = np.array([[3, 11], [11, 15]], dtype=np.int32)
+    w = np.array([[0.75, 0.25], [0.5, 0.5]])
+    el, sw = OM.expert_list(ids, w)
+    el_dev = np.zeros(1 + T * m.k, dtype=np.int32)
+    el_dev[0] = len(el)
+    el_dev[1:1 + len(el)] = el
+    sw_dev = np.zeros((T * m.k, T), dtype=np.float32)
+    sw_dev[:len(el)] = sw
+    for shared in (dw["shared"], None):
+        yd, hd = ops.moe_expert_gemv_mxfp4(P.to_dev_bf16(x), dw["w13c"], dw["w13s"], dw["w2c"], dw["w2s"],
+                                           P.to_dev(el_dev), P.to_dev(sw_dev), m.k, shared=shared)
+        get = lambda e: (lw["w13c"][e], lw["w13s"][e], lw["w2c"][e], lw["w2s"][e])
+        y_ref = P.moe_y_ref(x, ids, w, get, lw["shared"] if shared is not None else None, m.I)
+        ok, worst = C.fp_close(P.np_(yd), y_ref)
+        assert ok, worst
+        assert hd is None
+
+
+def test_router_ties_resolve_to_lowest_id(ops):
+    H, E, k = 256, 64, 8
+    w = inputs.normal_f32((4,), (E, H), 0.02)
+    for dup in ([5, 9, 40], [60, 61, 62, 63]):
+        w[dup] = w[dup[0]] + 1.0                            # identical rows with the largest logits
+    x = np.full((2, H), 0x3F80, dtype=np.uint16)
+    r = ops.moe_route_topk(P.to_dev_bf16(x), P.to_dev(w), k)
+    ids = P.np_(r["topk_ids"])
+    lg = P.np_(r["logits"])
+    assert lg[0, 5] == lg[0, 9] == lg[0, 40] and lg[0, 60] == lg[0, 63]
+    order = sorted(range(E), key=lambda e: (-lg[0, e], e))[:k]
+    assert list(ids[0]) == order and list(ids[1]) == order
+
+
+def test_router_k_equals_e_and_k_one(ops):
+    H = 64
+    for E, k in ((8, 8), (16, 1), (1024, 8)):
+        w = inputs.normal_f32((6, E), (E, H), 0.05)
+        x = inputs.normal_bf16((7, E), (3, H), 1.0)
+        r = ops.moe_route_topk(P.to_dev_bf16(x), P.to_dev(w), k)
+        P.check_routing(x, w.astype(np.float64), k, P.np_(r["topk_ids"]), P.np_(r["topk_w"]),
+                        P.np_(r["expert_list"]), P.np_(r["slot_w"]), P.np_(r["logits"]))
+
+
+@pytest.mark.parametrize("T", [1, 2, 4])
+@pytest.mark.parametrize("with_shared", [False, True])
+def test_planted_experts_bit_exact(ops, T, with_shared):
+    H, I, E = 2560, 768, 4
+    c13, s13, c2, s2 = P.planted_exact_layer(H, I, E + 1, seed=T)
+    wr = inputs.normal_f32((8, T), (E, H), 0.02)
+    xi = np.random.default_rng(T).integers(1, 3, size=(T, H))
+    x = torch.from_numpy(xi.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    xd = P.to_dev_bf16(x)
+    r = ops.moe_route_topk(xd, P.to_dev(wr), 1)
+    shared = tuple(P.to_dev(a[E]) for a in (c13, s13, c2, s2)) if with_shared else None
+    y, _ = ops.moe_expert_gemv_mxfp4(xd, P.to_dev(c13[:E]), P.to_dev(s13[:E]), P.to_dev(c2[:E]), P.to_dev(s2[:E]),
+                                     r["expert_list"], r["slot_w"], 1, shared=shared)
+    ids = P.np_(r["topk_ids"])[:, 0]
+    W = F.dequant_mxfp4(c13, s13, H)                      # exact multiples of 1/8
+    want = np.zeros((T, H))
+    for t in range(T):
+        experts = [ids[t]] + ([E] if with_shared else [])
+        for e in experts:
+            g = (W[e, :I] * 8).astype(np.int64) @ xi[t] / 8.0
+            want[t, :I] += g * xi[t, np.arange(I) % H]
+    assert np.array_equal(P.np_(y).astype(np.float64), want)
+
+
+# ----------------------------------------------------------------------------- Ling shape
+
+
+@pytest.fixture(scope="module")
+def ling(ops):
+    wl = configs.MOE_LAYER
+    lw = inputs.layer_weights(wl, 0)
+    dw = P.layer_to_dev(lw)
+    torch.cuda.synchronize()
+    return wl, lw, dw
+
+
+def test_ling_layer_one_token(ops, ling):
+    wl, lw, dw = ling
+    worst = 0.0
+    for step in range(6):
+        x = inputs.activations(wl, step)
+        res = inputs.normal_bf16((wl.seed, 99, step), (1, wl.moe.H), 1.0)
+        r, y, h = run_layer(ops, wl, dw, x, res)
+        assert int(r["expert_list"][0]) == 8
+        worst = max(worst, check_layer(wl, lw, x, res, r, y, h)[1])
+    print(f"worst y error {worst:.2e} x RMS")
+
+
+def test_ling_verify_pass_random_tokens(ops, ling):
+    wl, lw, dw = ling
+    vw = configs.VERIFY
+    for step in range(3):
+        x = inputs.normal_bf16((vw.seed, inputs.T_X, step), (4, wl.moe.H), 1.0)
+        res = inputs.normal_bf16((vw.seed, 99, step), (4, wl.moe.H), 1.0)
+        r, y, h = run_layer(ops, wl, dw, x, res)
+        D = int(r["expert_list"][0])
+        assert 24 <= D <= 32, D
+        check_layer(wl, lw, x, res, r, y, h)
+
+
+def test_ling_verify_pass_overlapping_tokens(ops, ling):
+    wl, lw, dw = ling
+    vw = configs.VERIFY
+    x = inputs.overlapping_activations(vw, 0)
+    res = inputs.normal_bf16((vw.seed, 98), (4, wl.moe.H), 1.0)
+    r, y, h = run_layer(ops, wl, dw, x, res)
+    D = int(r["expert_list"][0])
+    assert D < 32                       # tokens share experts
+    check_layer(wl, lw, x, res, r, y, h)
+
+
+def test_identical_tokens_give_identical_rows(ops, ling):
+    wl, lw, dw = ling
+    x = np.repeat(inputs.activations(wl, 7), 4, axis=0)
+    res = np.repeat(inputs.normal_bf16((5,), (1, wl.moe.H), 1.0), 4, axis=0)
+    r, y, h = run_layer(ops, wl, dw, x, res)
+    assert int(r["expert_list"][0]) == 8
+    for t in range(1, 4):
+        assert np.array_equal(y[t], y[0]) and np.array_equal(h[t], h[0])
+        assert np.array_equal(r["topk_ids"][t], r["topk_ids"][0])
+    r1, y1, h1 = run_layer(ops, wl, dw, x[:1], res[:1])
+    np.testing.assert_array_equal(r1["topk_ids"][0], r["topk_ids"][0])
+    assert C.fp_close(y1, y[:1])[0]
+
+
+def test_layer_is_deterministic(ops, ling):
+    wl, lw, dw = ling
+    x = inputs.normal_bf16((31,), (4, wl.moe.H), 1.0)
+    res = inputs.normal_bf16((32,), (4, wl.moe.H), 1.0)
+    first = run_layer(ops, wl, dw, x, res)
+    for _ in range(10):
+        again = run_layer(ops, wl, dw, x, res)
+        assert np.array_equal(first[1], again[1]) and np.array_equal(first[2], again[2])
+        for key in first[0]:
+            assert np.array_equal(first[0][key], again[0][key])

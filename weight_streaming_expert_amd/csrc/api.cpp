@@ -1,0 +1,262 @@
+// C ABI of libwsx.so: host-side argument validation, workspace layout and
+// launch sequencing.  Every check runs before anything is enqueued; on an
+// error no work is enqueued and outputs are untouched.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "wsx_internal.h"
+
+namespace {
+
+using namespace wsx;
+
+inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+inline bool a16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline wsx_status hip_status(hipError_t e) { return e == hipSuccess ? WSX_OK : WSX_ERR_HIP; }
+
+struct MoeWs {
+  size_t counter, logits, a, total;
+};
+MoeWs moe_ws(int T, int I, int E, int k) {
+  MoeWs w;
+  w.counter = 0;
+  w.logits = 256;
+  w.a = align256(w.logits + (size_t)T * E * 4);
+  w.total = align256(w.a + (size_t)(T * k + 1) * T * I * 4);
+  return w;
+}
+size_t head_ws_bytes() { return 256 + (size_t)2 * kHeadMaxGrid * WSX_MAX_T * 4; }
+
+struct StepWs {
+  MoeWs moe;
+  size_t moe_base, head, u, h0, h1, ids, w, el, sw, total;
+};
+StepWs step_ws(int T, int H, int I, int E, int k) {
+  StepWs s;
+  s.moe = moe_ws(T, I, E, k);
+  s.moe_base = 0;
+  s.head = align256(s.moe.total);
+  s.u = align256(s.head + head_ws_bytes());
+  s.h0 = align256(s.u + (size_t)T * H * 2);
+  s.h1 = align256(s.h0 + (size_t)T * H * 2);
+  s.ids = align256(s.h1 + (size_t)T * H * 2);
+  s.w = align256(s.ids + (size_t)T * k * 4);
+  s.el = align256(s.w + (size_t)T * k * 4);
+  s.sw = align256(s.el + (size_t)(1 + T * k) * 4);
+  s.total = align256(s.sw + (size_t)T * k * T * 4);
+  return s;
+}
+
+wsx_status check_tk(int T, int k, int E) {
+  if (T < 1 || k < 1 || E < 1 || k > E) return WSX_ERR_SHAPE;
+  if (T > WSX_MAX_T || k > WSX_MAX_K || E > WSX_MAX_E) return WSX_ERR_UNSUPPORTED;
+  return WSX_OK;
+}
+
+wsx_status check_ws(const void* ws, size_t have, size_t need) {
+  if (!ws) return WSX_ERR_WORKSPACE;
+  if (((uintptr_t)ws & 255u) != 0) return WSX_ERR_ALIGN;
+  if (have < need) return WSX_ERR_WORKSPACE;
+  return WSX_OK;
+}
+
+wsx_status check_router(const uint16_t* x, const void* w_router, int router_dtype, int T, int H, int E, int k) {
+  if (!x || !w_router) return WSX_ERR_NULL;
+  if (router_dtype != WSX_DTYPE_BF16 && router_dtype != WSX_DTYPE_F32) return WSX_ERR_DTYPE;
+  wsx_status st = check_tk(T, k, E);
+  if (st != WSX_OK) return st;
+  if (H < 32 || H % 32) return WSX_ERR_SHAPE;
+  if (!router_shape_supported(router_dtype, H)) return WSX_ERR_UNSUPPORTED;
+  if (!a16(x) || !a16(w_router)) return WSX_ERR_ALIGN;
+  return WSX_OK;
+}
+
+// Weights and shapes of the expert stage (the expert list is checked by the caller).
+wsx_status check_experts(const uint16_t* x, const uint8_t* w13c, const uint8_t* w13s, const uint8_t* w2c,
+                         const uint8_t* w2s, const uint8_t* sh13c, const uint8_t* sh13s, const uint8_t* sh2c,
+                         const uint8_t* sh2s, int T, int H, int I, int E, int k) {
+  if (!x || !w13c || !w13s || !w2c || !w2s) return WSX_ERR_NULL;
+  const int nsh = (sh13c != nullptr) + (sh13s != nullptr) + (sh2c != nullptr) + (sh2s != nullptr);
+  if (nsh != 0 && nsh != 4) return WSX_ERR_NULL;
+  wsx_status st = check_tk(T, k, E);
+  if (st != WSX_OK) return st;
+  if (H < 32 || I < 32 || H % 32 || I % 32) return WSX_ERR_SHAPE;
+  if (!experts_shape_supported(H, I)) return WSX_ERR_UNSUPPORTED;
+  if (!a16(x) || !a16(w13c) || !a16(w2c) || (sh13c && (!a16(sh13c) || !a16(sh2c)))) return WSX_ERR_ALIGN;
+  return WSX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t wsx_moe_workspace_bytes(int T, int H, int I, int E, int k) {
+  (void)H;
+  if (T < 1 || T > WSX_MAX_T || k < 1 || k > WSX_MAX_K || E < 1 || E > WSX_MAX_E || I < 0) return 0;
+  return moe_ws(T, I, E, k).total;
+}
+
+size_t wsx_lm_head_workspace_bytes(int T, int V, int K) {
+  (void)T; (void)V; (void)K;
+  return head_ws_bytes();
+}
+
+size_t wsx_decode_step_workspace_bytes(int T, int H, int I, int E, int k, int V) {
+  (void)V;
+  if (T < 1 || T > WSX_MAX_T || k < 1 || k > WSX_MAX_K || E < 1 || E > WSX_MAX_E || I < 0 || H < 0) return 0;
+  return step_ws(T, H, I, E, k).total;
+}
+
+wsx_status moe_route_topk(const uint16_t* x, const void* w_router, int router_dtype, int T, int H, int E, int k,
+                          int32_t* topk_ids, float* topk_w, int32_t* expert_list, float* slot_w, float* logits_out,
+                          void* ws, size_t ws_bytes, void* stream) {
+  wsx_status st = check_router(x, w_router, router_dtype, T, H, E, k);
+  if (st != WSX_OK) return st;
+  if (!topk_ids || !topk_w || !expert_list || !slot_w) return WSX_ERR_NULL;
+  if ((st = check_ws(ws, ws_bytes, moe_ws(T, 32, E, k).a)) != WSX_OK) return st;
+  const MoeWs L = moe_ws(T, 32, E, k);
+  float* logits = logits_out ? logits_out : reinterpret_cast<float*>((char*)ws + L.logits);
+  return hip_status(launch_router(router_dtype, w_router, E, H, k, x, T, 0, nullptr, logits, topk_ids, topk_w,
+                                  expert_list, slot_w, reinterpret_cast<unsigned*>((char*)ws + L.counter), S(stream)));
+}
+
+wsx_status moe_expert_gemv_mxfp4(const uint16_t* x, const uint8_t* w13_codes, const uint8_t* w13_scales,
+                                 const uint8_t* w2_codes, const uint8_t* w2_scales, const uint8_t* sh13_codes,
+                                 const uint8_t* sh13_scales, const uint8_t* sh2_codes, const uint8_t* sh2_scales,
+                                 const int32_t* expert_list, const float* slot_w, int T, int H, int I, int E, int k,
+                                 const uint16_t* residual, float* out_y, uint16_t* out_h, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  if (!expert_list || !slot_w) return WSX_ERR_NULL;
+  wsx_status st = check_experts(x, w13_codes, w13_scales, w2_codes, w2_scales, sh13_codes, sh13_scales, sh2_codes,
+                                sh2_scales, T, H, I, E, k);
+  if (st != WSX_OK) return st;
+  if (out_h && !residual) return WSX_ERR_NULL;
+  const MoeWs L = moe_ws(T, I, E, k);
+  if ((st = check_ws(ws, ws_bytes, L.total)) != WSX_OK) return st;
+  float* a = reinterpret_cast<float*>((char*)ws + L.a);
+  hipError_t e = launch_gateup(x, T, H, I, E, k, w13_codes, w13_scales, sh13_codes, sh13_scales, expert_list, a,
+                               S(stream));
+  if (e != hipSuccess) return WSX_ERR_HIP;
+  return hip_status(launch_down(T, H, I, E, k, w2_codes, w2_scales, sh2_codes, sh2_scales, expert_list, slot_w, a,
+                                residual, out_y, out_h, nullptr, S(stream)));
+}
+
+wsx_status lm_head_quantize_fp8(const uint16_t* w, int V, int K, uint8_t* q, float* row_scale, void* stream) {
+  if (!w || !q || !row_scale) return WSX_ERR_NULL;
+  if (V < 1 || K < 32 || K % 32) return WSX_ERR_SHAPE;
+  if (K > 16384) return WSX_ERR_UNSUPPORTED;
+  if (!a16(w) || !a16(q)) return WSX_ERR_ALIGN;
+  return hip_status(launch_quant_fp8(w, V, K, q, row_scale, S(stream)));
+}
+
+static wsx_status head_common(int wt, const void* W, const float* s, int V, int K, const uint16_t* x, int T,
+                              float* logits, int32_t* argmax, void* ws, size_t ws_bytes, void* stream) {
+  if (!W || !x || !argmax || (wt == 0 && !s)) return WSX_ERR_NULL;
+  if (V < 1 || K < 32 || K % 32 || T < 1) return WSX_ERR_SHAPE;
+  if (T > WSX_MAX_T || !head_shape_supported(wt, K)) return WSX_ERR_UNSUPPORTED;
+  if (!a16(W) || !a16(x)) return WSX_ERR_ALIGN;
+  wsx_status st = check_ws(ws, ws_bytes, head_ws_bytes());
+  if (st != WSX_OK) return st;
+  return hip_status(launch_lm_head(wt, W, s, V, K, x, T, 0, nullptr, logits, argmax, ws, S(stream)));
+}
+
+wsx_status lm_head_gemv_fp8_argmax(const uint8_t* q, const float* row_scale, int V, int K, const uint16_t* x, int T,
+                                   float* logits, int32_t* argmax, void* ws, size_t ws_bytes, void* stream) {
+  return head_common(0, q, row_scale, V, K, x, T, logits, argmax, ws, ws_bytes, stream);
+}
+
+wsx_status lm_head_gemv_bf16_argmax(const uint16_t* w, int V, int K, const uint16_t* x, int T, float* logits,
+                                    int32_t* argmax, void* ws, size_t ws_bytes, void* stream) {
+  return head_common(1, w, nullptr, V, K, x, T, logits, argmax, ws, ws_bytes, stream);
+}
+
+wsx_status moe_decode_step(const uint16_t* h_in, int T, const wsx_moe_stack* sk, const uint8_t* head_q,
+                           const float* head_scale, int V, uint16_t* h_out, float* logits, int32_t* argmax,
+                           uint16_t* h_trace, uint16_t* u_trace, int32_t* ids_trace, float* w_trace, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (!sk || !h_in || !head_q || !head_scale || !h_out || !argmax) return WSX_ERR_NULL;
+  if (sk->L < 1) return WSX_ERR_SHAPE;
+  const int H = sk->H, I = sk->I, E = sk->E, k = sk->k, L = sk->L;
+  wsx_status st = check_router(h_in, sk->w_router, sk->router_dtype, T, H, E, k);
+  if (st != WSX_OK) return st;
+  st = check_experts(h_in, sk->w13_codes, sk->w13_scales, sk->w2_codes, sk->w2_scales, sk->sh13_codes,
+                     sk->sh13_scales, sk->sh2_codes, sk->sh2_scales, T, H, I, E, k);
+  if (st != WSX_OK) return st;
+  if (V < 1) return WSX_ERR_SHAPE;
+  if (!head_shape_supported(0, H)) return WSX_ERR_UNSUPPORTED;
+  if (!a16(head_q) || !a16(h_out)) return WSX_ERR_ALIGN;
+  if ((h_trace && !a16(h_trace)) || (u_trace && !a16(u_trace))) return WSX_ERR_ALIGN;
+  const StepWs W = step_ws(T, H, I, E, k);
+  if ((st = check_ws(ws, ws_bytes, W.total)) != WSX_OK) return st;
+
+  char* base = reinterpret_cast<char*>(ws);
+  unsigned* counter = reinterpret_cast<unsigned*>(base + W.moe.counter);
+  float* rlogits = reinterpret_cast<float*>(base + W.moe.logits);
+  float* a = reinterpret_cast<float*>(base + W.moe.a);
+  int32_t* el = reinterpret_cast<int32_t*>(base + W.el);
+  float* sw = reinterpret_cast<float*>(base + W.sw);
+  uint16_t* ping[2] = {reinterpret_cast<uint16_t*>(base + W.h0), reinterpret_cast<uint16_t*>(base + W.h1)};
+  const size_t TH = (size_t)T * H;
+  const size_t esz = sk->router_dtype == WSX_DTYPE_F32 ? 4 : 2;
+  const size_t r_stride = (size_t)E * H * esz;
+  const size_t c13 = (size_t)E * 2 * I * (H / 2), s13 = (size_t)E * 2 * I * (H / 32);
+  const size_t c2 = (size_t)E * H * (I / 2), s2 = (size_t)E * H * (I / 32);
+  const size_t sc13 = (size_t)2 * I * (H / 2), ss13 = (size_t)2 * I * (H / 32);
+  const size_t sc2 = (size_t)H * (I / 2), ss2 = (size_t)H * (I / 32);
+  const bool sh = sk->sh13_codes != nullptr;
+  hipStream_t s = S(stream);
+
+  const uint16_t* h_cur = h_in;
+  if (h_trace) {
+    // h_0 is the input itself; record it
+    if (hipMemcpyAsync(h_trace, h_in, TH * 2, hipMemcpyDeviceToDevice, s) != hipSuccess) return WSX_ERR_HIP;
+  }
+  for (int l = 0; l < L; ++l) {
+    uint16_t* u = u_trace ? u_trace + (size_t)l * TH : reinterpret_cast<uint16_t*>(base + W.u);
+    int32_t* ids = ids_trace ? ids_trace + (size_t)l * T * k : reinterpret_cast<int32_t*>(base + W.ids);
+    float* tw = w_trace ? w_trace + (size_t)l * T * k : reinterpret_cast<float*>(base + W.w);
+    uint16_t* h_next = h_trace ? h_trace + (size_t)(l + 1) * TH : (l == L - 1 ? h_out : ping[l & 1]);
+    uint16_t* h_next2 = (h_trace && l == L - 1) ? h_out : nullptr;
+    const char* wr = reinterpret_cast<const char*>(sk->w_router) + (size_t)l * r_stride;
+    hipError_t e = launch_router(sk->router_dtype, wr, E, H, k, h_cur, T, 1, u, rlogits, ids, tw, el, sw, counter, s);
+    if (e != hipSuccess) return WSX_ERR_HIP;
+    e = launch_gateup(u, T, H, I, E, k, sk->w13_codes + (size_t)l * c13, sk->w13_scales + (size_t)l * s13,
+                      sh ? sk->sh13_codes + (size_t)l * sc13 : nullptr, sh ? sk->sh13_scales + (size_t)l * ss13 : nullptr,
+                      el, a, s);
+    if (e != hipSuccess) return WSX_ERR_HIP;
+    e = launch_down(T, H, I, E, k, sk->w2_codes + (size_t)l * c2, sk->w2_scales + (size_t)l * s2,
+                    sh ? sk->sh2_codes + (size_t)l * sc2 : nullptr, sh ? sk->sh2_scales + (size_t)l * ss2 : nullptr,
+                    el, sw, a, h_cur, nullptr, h_next, h_next2, s);
+    if (e != hipSuccess) return WSX_ERR_HIP;
+    h_cur = h_next;
+  }
+  uint16_t* u_head = u_trace ? u_trace + (size_t)L * TH : nullptr;
+  return hip_status(launch_lm_head(0, head_q, head_scale, V, H, h_cur, T, 1, u_head, logits, argmax,
+                                   base + W.head, s));
+}
+
+const char* wsx_status_string(wsx_status s) {
+  switch (s) {
+    case WSX_OK: return "ok";
+    case WSX_ERR_NULL: return "required pointer is NULL";
+    case WSX_ERR_SHAPE: return "size out of range or not a multiple of 32";
+    case WSX_ERR_ALIGN: return "pointer not 16-byte aligned (workspace: 256-byte)";
+    case WSX_ERR_UNSUPPORTED: return "shape valid but not supported by the compiled kernels";
+    case WSX_ERR_WORKSPACE: return "workspace missing or too small";
+    case WSX_ERR_DTYPE: return "unknown dtype code";
+    case WSX_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+#define WSX_STR2(x) #x
+#define WSX_STR(x) WSX_STR2(x)
+const char* wsx_build_info(void) {
+  return "libwsx arch=gfx950 hip=" WSX_STR(HIP_VERSION_MAJOR) "." WSX_STR(HIP_VERSION_MINOR)
+         " kernels=router_topk<bf16|f32,T1-4>,moe_gateup<T1-4;valu-dot2>,moe_down<T1-4;valu>,"
+         "lm_head<fp8|bf16,T1-4>,quant_fp8";
+}
+
+}  // extern "C"

@@ -1,0 +1,444 @@
+// Dense row GEMVs of the decode path on gfx950:
+//   * the MoE router: logits = Wr x (bf16 or fp32 weights), then, in the last
+//     workgroup to finish, the per-token top-k, the softmax over the selected
+//     logits and the compact expert list ([saipien] "Why one user waits on
+//     weights": 8 of 512 routed experts per token; [saipien] "Draft three
+//     tokens, verify four": up to 32 distinct experts for 4 positions);
+//   * the LM head: logits = s .* (Wq x) over FP8 E4M3 rows with a per-row
+//     scale, or over BF16 rows, with a fused two-pass greedy argmax ([saipien]
+//     "Stop hauling the vocabulary in full precision"; [ncij] "What happens
+//     on a real workload?" for greedy decoding).
+//
+// Layout of the work: a wavefront streams 4 rows at a time, 16 lanes per row.
+// Each lane owns the 16-byte granules c, c+16, c+32, ... of its row (c = lane
+// mod 16), so one wavefront load instruction reads 4 x 256 contiguous bytes.
+// The activation granules a lane needs are the same for every row, so for a
+// single token they are held in registers for the whole kernel; with several
+// tokens they are read from LDS.  Row sums are formed by a fixed DPP tree
+// within each 16-lane row, identical for every row, so equal rows give
+// bit-identical logits and ties resolve exactly to the lower index.
+#include "wsx_device.h"
+#include "wsx_internal.h"
+
+namespace wsx {
+
+enum WType { W_FP8 = 0, W_BF16 = 1, W_F32 = 2 };
+
+template <int WT> struct WTraits;
+template <> struct WTraits<W_FP8> { static constexpr int EPG = 16; static constexpr int ESZ = 1; };
+template <> struct WTraits<W_BF16> { static constexpr int EPG = 8; static constexpr int ESZ = 2; };
+template <> struct WTraits<W_F32> { static constexpr int EPG = 4; static constexpr int ESZ = 4; };
+
+template <int WT>
+__device__ __forceinline__ float granule_dot(uint4 w, const uint32_t* xp) {
+  if constexpr (WT == W_FP8) return fp8_granule_dot(w, xp);
+  else if constexpr (WT == W_BF16) return bf16_granule_dot(w, xp);
+  else return f32_granule_dot(w, xp);
+}
+
+constexpr int kMaxK = 8192;          // LDS activation stage: T * K bf16 <= 64 KiB
+
+// Stage the activations [T][K] as bf16 in LDS.  With `norm` set the input is
+// the residual stream h and the staged value is u = RNE_bf16(h / sqrt(mean(h^2)
+// + 1e-6)), per token; workgroup 0 also writes u to u_out when it is non-null.
+// The sum of squares uses one fixed order, so every workgroup derives the
+// same u.
+template <int T, int NT>
+__device__ __forceinline__ void stage_input(const uint16_t* __restrict__ x, int K, bool norm, uint16_t* u_out,
+                                            uint16_t* xs, float* red) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < T * K; i += NT) xs[i] = x[i];
+  if (!norm) { __syncthreads(); return; }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    float ss = 0.f;
+    for (int i = tid; i < K; i += NT) {
+      float v = bf16_bits_to_f32(xs[t * K + i]);
+      ss = fmaf(v, v, ss);
+    }
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) red[t * (NT / 64) + (tid >> 6)] = ss;
+  }
+  __syncthreads();
+  float r[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    float s = 0.f;
+    for (int w = 0; w < NT / 64; ++w) s += red[t * (NT / 64) + w];
+    r[t] = 1.0f / sqrtf(s / (float)K + 1e-6f);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+    for (int i = tid; i < K; i += NT) {
+      uint16_t u = f32_to_bf16_rne(bf16_bits_to_f32(xs[t * K + i]) * r[t]);
+      xs[t * K + i] = u;
+      if (blockIdx.x == 0 && u_out) u_out[t * K + i] = u;
+    }
+  __syncthreads();
+}
+
+// Dot products of up to UNR row groups (4 rows each) for T tokens.
+// Row index of this lane for group u: rg[u] * 4 + (lane >> 4).
+template <int WT, int T, int GPL, int UNR>
+__device__ __forceinline__ void rows_dot(const uint8_t* __restrict__ W, size_t row_bytes, int V, int G, const int* rg,
+                                         const uint32_t (*xr)[WTraits<WT>::EPG / 2], const uint32_t* xs32, int K,
+                                         float (*acc)[T]) {
+  constexpr int DW = WTraits<WT>::EPG / 2;   // dwords of bf16 activations per granule
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15;
+  uint4 wv[UNR][GPL];
+#pragma unroll
+  for (int u = 0; u < UNR; ++u) {
+    const int row = rg[u] * 4 + (lane >> 4);
+    const bool ok = row < V;
+#pragma unroll
+    for (int j = 0; j < GPL; ++j) {
+      const int g = c + 16 * j;
+      wv[u][j] = (ok && g < G) ? ld16(W + (size_t)row * row_bytes + (size_t)g * 16) : make_uint4(0, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < UNR; ++u)
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[u][t] = 0.f;
+#pragma unroll
+  for (int j = 0; j < GPL; ++j) {
+    const int g = c + 16 * j;
+    if (g >= G) continue;
+    if constexpr (T == 1) {
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) acc[u][0] += granule_dot<WT>(wv[u][j], xr[j]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        uint32_t xp[DW];
+        const uint32_t* src = xs32 + (size_t)t * (K / 2) + (size_t)g * DW;
+#pragma unroll
+        for (int d = 0; d < DW; ++d) xp[d] = src[d];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) acc[u][t] += granule_dot<WT>(wv[u][j], xp);
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < UNR; ++u)
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[u][t] = sum16(acc[u][t]);
+}
+
+template <int WT, int GPL>
+__device__ __forceinline__ void load_x_regs(const uint32_t* xs32, int G, uint32_t (*xr)[WTraits<WT>::EPG / 2]) {
+  constexpr int DW = WTraits<WT>::EPG / 2;
+  const int c = threadIdx.x & 15;
+#pragma unroll
+  for (int j = 0; j < GPL; ++j) {
+    const int g = c + 16 * j;
+#pragma unroll
+    for (int d = 0; d < DW; ++d) xr[j][d] = (g < G) ? xs32[(size_t)g * DW + d] : 0u;
+  }
+}
+
+// ---------------------------------------------------------------- LM head
+
+template <int WT, int T, int GPL>
+__global__ void __launch_bounds__(256) lm_head_kernel(const uint8_t* __restrict__ W, const float* __restrict__ row_scale,
+                                                      int V, int K, const uint16_t* __restrict__ x, int norm,
+                                                      uint16_t* u_out, float* __restrict__ logits,
+                                                      int32_t* __restrict__ argmax, unsigned* counter, float* part_v,
+                                                      int* part_i) {
+  constexpr int NT = 256, UNR = 2, DW = WTraits<WT>::EPG / 2;
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
+  __shared__ float red[4 * T * 4];
+  __shared__ int flag;
+  stage_input<T, NT>(x, K, norm != 0, u_out, xs, red);
+  const uint32_t* xs32 = reinterpret_cast<const uint32_t*>(xs);
+  const int G = K / WTraits<WT>::EPG;
+  const size_t row_bytes = (size_t)K * WTraits<WT>::ESZ;
+  uint32_t xr[T == 1 ? GPL : 1][DW];
+  if constexpr (T == 1) load_x_regs<WT, GPL>(xs32, G, xr);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nwaves = gridDim.x * 4;
+  const int NG = (V + 3) / 4;
+  float bv[T];
+  int bi[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) { bv[t] = -INFINITY; bi[t] = 0x7FFFFFFF; }
+
+  for (int base = blockIdx.x * 4 + wave; base < NG; base += nwaves * UNR) {
+    int rg[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) rg[u] = base + u * nwaves;
+    float acc[UNR][T];
+    float sc[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int row = rg[u] * 4 + (lane >> 4);
+      sc[u] = (WT == W_FP8 && row < V && (lane & 15) == 0) ? row_scale[row] : 1.0f;
+    }
+    rows_dot<WT, T, GPL, UNR>(W, row_bytes, V, G, rg, xr, xs32, K, acc);
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int row = rg[u] * 4 + (lane >> 4);
+      if ((lane & 15) == 0 && row < V) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const float l = (WT == W_FP8) ? acc[u][t] * sc[u] : acc[u][t];
+          if (logits) logits[(size_t)t * V + row] = l;
+          if (better(l, row, bv[t], bi[t])) { bv[t] = l; bi[t] = row; }
+        }
+      }
+    }
+  }
+  // workgroup argmax, then the last workgroup reduces the per-workgroup partials
+  __shared__ float wv_[4][T];
+  __shared__ int wi_[4][T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    float v = bv[t];
+    int i = bi[t];
+    wave_argmax(v, i);
+    if (lane == 0) { wv_[wave][t] = v; wi_[wave][t] = i; }
+  }
+  __syncthreads();
+  if (threadIdx.x < T) {
+    const int t = threadIdx.x;
+    float v = wv_[0][t];
+    int i = wi_[0][t];
+    for (int w = 1; w < 4; ++w)
+      if (better(wv_[w][t], wi_[w][t], v, i)) { v = wv_[w][t]; i = wi_[w][t]; }
+    st_dev(part_v + (size_t)blockIdx.x * T + t, v);
+    st_dev(part_i + (size_t)blockIdx.x * T + t, i);
+  }
+  if (!last_block_arrived(counter, gridDim.x, &flag)) return;
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    float v = -INFINITY;
+    int i = 0x7FFFFFFF;
+    for (int b = threadIdx.x; b < (int)gridDim.x; b += NT) {
+      float ov = ld_dev(part_v + (size_t)b * T + t);
+      int oi = ld_dev(part_i + (size_t)b * T + t);
+      if (better(ov, oi, v, i)) { v = ov; i = oi; }
+    }
+    wave_argmax(v, i);
+    if (lane == 0) { wv_[wave][t] = v; wi_[wave][t] = i; }
+  }
+  __syncthreads();
+  if (threadIdx.x < T) {
+    const int t = threadIdx.x;
+    float v = wv_[0][t];
+    int i = wi_[0][t];
+    for (int w = 1; w < 4; ++w)
+      if (better(wv_[w][t], wi_[w][t], v, i)) { v = wv_[w][t]; i = wi_[w][t]; }
+    argmax[t] = i;
+  }
+}
+
+// ---------------------------------------------------------------- router + top-k
+
+constexpr int kRouterWaves = 1;   // one wavefront per workgroup spreads the 2.6 MB router over more CUs
+
+template <int WT, int T, int GPL>
+__global__ void __launch_bounds__(64 * kRouterWaves) router_topk_kernel(
+    const uint8_t* __restrict__ W, int E, int K, int k, const uint16_t* __restrict__ x, int norm, uint16_t* u_out,
+    float* logits, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, int32_t* __restrict__ expert_list,
+    float* __restrict__ slot_w, unsigned* counter) {
+  constexpr int NT = 64 * kRouterWaves, DW = WTraits<WT>::EPG / 2;
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
+  __shared__ float red[T * kRouterWaves * 4];
+  __shared__ int flag;
+  stage_input<T, NT>(x, K, norm != 0, u_out, xs, red);
+  const uint32_t* xs32 = reinterpret_cast<const uint32_t*>(xs);
+  const int G = K / WTraits<WT>::EPG;
+  const size_t row_bytes = (size_t)K * WTraits<WT>::ESZ;
+  uint32_t xr[T == 1 ? GPL : 1][DW];
+  if constexpr (T == 1) load_x_regs<WT, GPL>(xs32, G, xr);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int NG = (E + 3) / 4;
+  for (int g0 = blockIdx.x * kRouterWaves + wave; g0 < NG; g0 += gridDim.x * kRouterWaves) {
+    int rg[1] = {g0};
+    float acc[1][T];
+    rows_dot<WT, T, GPL, 1>(W, row_bytes, E, G, rg, xr, xs32, K, acc);
+    const int row = g0 * 4 + (lane >> 4);
+    if ((lane & 15) == 0 && row < E)
+#pragma unroll
+      for (int t = 0; t < T; ++t) st_dev(logits + (size_t)t * E + row, acc[0][t]);
+  }
+  if (!last_block_arrived(counter, gridDim.x, &flag)) return;
+
+  // ---- last workgroup: top-k per token, softmax over the selected logits,
+  //      then the compact ascending expert list and the slot weight table.
+  __shared__ int sel_id[WSX_MAX_T * WSX_MAX_K];
+  __shared__ float sel_w[WSX_MAX_T * WSX_MAX_K];
+  __shared__ int sel_first[WSX_MAX_T * WSX_MAX_K];
+  __shared__ int sel_rank[WSX_MAX_T * WSX_MAX_K];
+  __shared__ float sw_tab[WSX_MAX_T * WSX_MAX_K * WSX_MAX_T];
+  constexpr int kPerLane = WSX_MAX_E / 64;
+  for (int t = wave; t < T; t += kRouterWaves) {
+    float lv[kPerLane];
+    unsigned taken = 0;
+#pragma unroll
+    for (int m = 0; m < kPerLane; ++m) {
+      const int e = lane + 64 * m;
+      lv[m] = (e < E) ? ld_dev(logits + (size_t)t * E + e) : -INFINITY;
+    }
+    float top[WSX_MAX_K];
+    int topi[WSX_MAX_K];
+#pragma unroll
+    for (int j = 0; j < WSX_MAX_K; ++j) {
+      top[j] = -INFINITY;
+      topi[j] = 0;
+      if (j < k) {
+        float v = -INFINITY;
+        int i = 0x7FFFFFFF;
+#pragma unroll
+        for (int m = 0; m < kPerLane; ++m) {
+          const int e = lane + 64 * m;
+          if (e < E && !((taken >> m) & 1u) && better(lv[m], e, v, i)) { v = lv[m]; i = e; }
+        }
+        wave_argmax(v, i);
+        top[j] = v;
+        topi[j] = i;
+        if ((i & 63) == lane) taken |= 1u << (i >> 6);
+      }
+    }
+    float zs = 0.f, zl = 0.f;
+    int il = 0;
+#pragma unroll
+    for (int j = 0; j < WSX_MAX_K; ++j) {
+      if (j < k) {
+        const float z = __expf(top[j] - top[0]);
+        zs += z;
+        if (j == lane) { zl = z; il = topi[j]; }
+      }
+    }
+    if (lane < k) {
+      const float wj = zl / zs;
+      topk_ids[t * k + lane] = il;
+      topk_w[t * k + lane] = wj;
+      sel_id[t * k + lane] = il;
+      sel_w[t * k + lane] = wj;
+    }
+  }
+  __syncthreads();
+  const int n = T * k;
+  if (wave == 0) {
+    int id = (lane < n) ? sel_id[lane] : 0x7FFFFFFF;
+    int first = lane < n;
+    for (int j = 0; j < n; ++j) if (j < lane && sel_id[j] == id) first = 0;
+    if (lane < n) sel_first[lane] = first;
+    for (int e = lane; e < n * T; e += 64) sw_tab[e] = 0.f;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    int id = (lane < n) ? sel_id[lane] : 0x7FFFFFFF;
+    int rank = 0, n_active = 0;
+    for (int j = 0; j < n; ++j) {
+      rank += (sel_first[j] && sel_id[j] < id);
+      n_active += sel_first[j];
+    }
+    if (lane < n) sel_rank[lane] = rank;
+    if (lane == 0) expert_list[0] = n_active;
+    if (lane < n && sel_first[lane]) expert_list[1 + rank] = id;
+    if (lane < n) sw_tab[rank * T + lane / k] = sel_w[lane];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < n * T; e += NT) slot_w[e] = sw_tab[e];
+}
+
+// ---------------------------------------------------------------- launchers
+
+template <int WT, int T>
+static hipError_t launch_head_t(const void* W, const float* s, int V, int K, const uint16_t* x, int norm, uint16_t* u_out,
+                                float* logits, int32_t* argmax, unsigned* counter, float* pv, int* pi, int grid,
+                                hipStream_t st) {
+  const int G = K / WTraits<WT>::EPG;
+  const int gpl = (G + 15) / 16;
+#define WSX_HEAD_CASE(N)                                                                                        \
+  case N:                                                                                                       \
+    lm_head_kernel<WT, T, N><<<grid, 256, (size_t)T * K * 2, st>>>((const uint8_t*)W, s, V, K, x, norm, u_out, logits, argmax, \
+                                                   counter, pv, pi);                                            \
+    break;
+  switch (gpl) {
+    WSX_HEAD_CASE(1) WSX_HEAD_CASE(2) WSX_HEAD_CASE(4) WSX_HEAD_CASE(5) WSX_HEAD_CASE(8) WSX_HEAD_CASE(10)
+    WSX_HEAD_CASE(16) WSX_HEAD_CASE(20) WSX_HEAD_CASE(32)
+    default: return hipErrorInvalidValue;
+  }
+#undef WSX_HEAD_CASE
+  return hipGetLastError();
+}
+
+bool head_shape_supported(int wt, int K) {
+  const int epg = wt == 0 ? 16 : 8;
+  if (K % 32 != 0 || K > kMaxK) return false;
+  const int gpl = (K / epg + 15) / 16;
+  return gpl == 1 || gpl == 2 || gpl == 4 || gpl == 5 || gpl == 8 || gpl == 10 || gpl == 16 || gpl == 20 || gpl == 32;
+}
+
+int head_grid(int V) {
+  const int NG = (V + 3) / 4;
+  const int waves = (NG + 1) / 2;
+  int g = (waves + 3) / 4;
+  return g < 1 ? 1 : (g > kHeadMaxGrid ? kHeadMaxGrid : g);
+}
+
+hipError_t launch_lm_head(int wt, const void* W, const float* s, int V, int K, const uint16_t* x, int T, int norm,
+                          uint16_t* u_out, float* logits, int32_t* argmax, void* ws, hipStream_t st) {
+  unsigned* counter = reinterpret_cast<unsigned*>(ws);
+  const int grid = head_grid(V);
+  float* pv = reinterpret_cast<float*>((char*)ws + 256);
+  int* pi = reinterpret_cast<int*>((char*)ws + 256 + (size_t)kHeadMaxGrid * WSX_MAX_T * 4);
+#define WSX_T_CASE(WTV, TV) \
+  if (wt == WTV && T == TV) return launch_head_t<WTV, TV>(W, s, V, K, x, norm, u_out, logits, argmax, counter, pv, pi, grid, st);
+  WSX_T_CASE(W_FP8, 1) WSX_T_CASE(W_FP8, 2) WSX_T_CASE(W_FP8, 3) WSX_T_CASE(W_FP8, 4)
+  WSX_T_CASE(W_BF16, 1) WSX_T_CASE(W_BF16, 2) WSX_T_CASE(W_BF16, 3) WSX_T_CASE(W_BF16, 4)
+#undef WSX_T_CASE
+  return hipErrorInvalidValue;
+}
+
+template <int WT, int T>
+static hipError_t launch_router_t(const void* W, int E, int K, int k, const uint16_t* x, int norm, uint16_t* u_out,
+                                  float* logits, int32_t* ids, float* w, int32_t* el, float* sw, unsigned* counter,
+                                  hipStream_t st) {
+  const int G = K / WTraits<WT>::EPG;
+  const int gpl = (G + 15) / 16;
+  const int NG = (E + 3) / 4;
+  const int grid = (NG + kRouterWaves - 1) / kRouterWaves;
+#define WSX_R_CASE(N)                                                                                              \
+  case N:                                                                                                          \
+    router_topk_kernel<WT, T, N><<<grid, 64 * kRouterWaves, (size_t)T * K * 2, st>>>((const uint8_t*)W, E, K, k, x, norm, u_out, \
+                                                                      logits, ids, w, el, sw, counter);            \
+    break;
+  switch (gpl) {
+    WSX_R_CASE(1) WSX_R_CASE(2) WSX_R_CASE(4) WSX_R_CASE(5) WSX_R_CASE(8) WSX_R_CASE(10) WSX_R_CASE(16)
+    WSX_R_CASE(20) WSX_R_CASE(32) WSX_R_CASE(40)
+    default: return hipErrorInvalidValue;
+  }
+#undef WSX_R_CASE
+  return hipGetLastError();
+}
+
+bool router_shape_supported(int router_dtype, int K) {
+  const int epg = router_dtype == WSX_DTYPE_F32 ? 4 : 8;
+  if (K % 32 != 0 || K > kMaxK) return false;
+  const int gpl = (K / epg + 15) / 16;
+  return gpl == 1 || gpl == 2 || gpl == 4 || gpl == 5 || gpl == 8 || gpl == 10 || gpl == 16 || gpl == 20 ||
+         gpl == 32 || gpl == 40;
+}
+
+hipError_t launch_router(int router_dtype, const void* W, int E, int K, int k, const uint16_t* x, int T, int norm,
+                         uint16_t* u_out, float* logits, int32_t* ids, float* w, int32_t* el, float* sw,
+                         unsigned* counter, hipStream_t st) {
+#define WSX_T_CASE(DT, WTV, TV) \
+  if (router_dtype == DT && T == TV) return launch_router_t<WTV, TV>(W, E, K, k, x, norm, u_out, logits, ids, w, el, sw, counter, st);
+  WSX_T_CASE(WSX_DTYPE_BF16, W_BF16, 1) WSX_T_CASE(WSX_DTYPE_BF16, W_BF16, 2)
+  WSX_T_CASE(WSX_DTYPE_BF16, W_BF16, 3) WSX_T_CASE(WSX_DTYPE_BF16, W_BF16, 4)
+  WSX_T_CASE(WSX_DTYPE_F32, W_F32, 1) WSX_T_CASE(WSX_DTYPE_F32, W_F32, 2)
+  WSX_T_CASE(WSX_DTYPE_F32, W_F32, 3) WSX_T_CASE(WSX_DTYPE_F32, W_F32, 4)
+#undef WSX_T_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace wsx

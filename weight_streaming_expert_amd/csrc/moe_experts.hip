@@ -1,0 +1,319 @@
+// Routed + shared SwiGLU experts with MXFP4 weights for batch-1 decode and the
+// 4-token verify pass, on gfx950.
+//
+// [saipien] "Why one user waits on weights": each token uses 8 of 512 routed
+// experts plus one shared expert, and MoE weight reads dominate decode time.
+// [saipien] "Kernels built for the shape you actually have": the routed
+// experts are narrow (intermediate size 768).
+//
+// Two launches per layer, both driven by the device-side expert list (the
+// host never learns which experts were chosen):
+//   gate/up  grid (I/16, T*k+1): workgroup (i-tile, slot) streams 16 gate rows
+//            and the 16 matching up rows of that slot's expert, dequantizes the
+//            E2M1 nibbles in registers with the hardware converter, applies the
+//            E8M0 block scale per 32 elements and writes a = silu(g) * u (fp32).
+//            Surplus workgroups (slots past the active count) exit at once.
+//   down     grid (H/8): workgroup owns 8 output rows and loops over every
+//            active slot (its 4 wavefronts take slots round-robin), then sums
+//            the four wavefront partials in a fixed order, adds the residual
+//            and rounds to bf16.  The order never depends on timing, so the
+//            result is bit-reproducible.
+#include "wsx_device.h"
+#include "wsx_internal.h"
+
+namespace wsx {
+
+// MX block (32 E2M1 codes) x 32 fp32 activations, unscaled.
+__device__ __forceinline__ float mx_block_dot_f32(uint4 c, const float* a) {
+  float s0 = 0.f, s1 = 0.f;
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    f32x2_t p0 = fp4x2_to_f32x2<0>(w[d]);
+    f32x2_t p1 = fp4x2_to_f32x2<1>(w[d]);
+    f32x2_t p2 = fp4x2_to_f32x2<2>(w[d]);
+    f32x2_t p3 = fp4x2_to_f32x2<3>(w[d]);
+    s0 = fmaf(p0.x, a[8 * d + 0], s0);
+    s1 = fmaf(p0.y, a[8 * d + 1], s1);
+    s0 = fmaf(p1.x, a[8 * d + 2], s0);
+    s1 = fmaf(p1.y, a[8 * d + 3], s1);
+    s0 = fmaf(p2.x, a[8 * d + 4], s0);
+    s1 = fmaf(p2.y, a[8 * d + 5], s1);
+    s0 = fmaf(p3.x, a[8 * d + 6], s0);
+    s1 = fmaf(p3.y, a[8 * d + 7], s1);
+  }
+  return s0 + s1;
+}
+
+// Resolve slot -> (codes, scales) of its expert; false if the slot is inactive
+// or its id is out of range (then the slot contributes nothing).
+__device__ __forceinline__ bool slot_expert(int slot, int n_active, bool has_sh, int E, const int32_t* expert_list,
+                                            const uint8_t* wc, const uint8_t* ws_, const uint8_t* shc,
+                                            const uint8_t* shs, size_t c_stride, size_t s_stride,
+                                            const uint8_t** C, const uint8_t** S) {
+  if (slot < n_active) {
+    const int e = expert_list[1 + slot];
+    if (e < 0 || e >= E) return false;
+    *C = wc + (size_t)e * c_stride;
+    *S = ws_ + (size_t)e * s_stride;
+    return true;
+  }
+  if (slot == n_active && has_sh) { *C = shc; *S = shs; return true; }
+  return false;
+}
+
+// ---------------------------------------------------------------- gate/up + SwiGLU
+
+template <int T, int NJ>
+__global__ void __launch_bounds__(256) moe_gateup_kernel(const uint16_t* __restrict__ x, int H, int I, int E, int max_slots,
+                                                         const uint8_t* __restrict__ w13c, const uint8_t* __restrict__ w13s,
+                                                         const uint8_t* __restrict__ sh13c, const uint8_t* __restrict__ sh13s,
+                                                         const int32_t* __restrict__ expert_list, float* __restrict__ a_out) {
+  const int slot = blockIdx.y;
+  int n_active = expert_list[0];
+  n_active = n_active < 0 ? 0 : (n_active > max_slots - 1 ? max_slots - 1 : n_active);
+  const bool has_sh = sh13c != nullptr;
+  const int i0 = blockIdx.x * 16;
+  const uint8_t *C, *S;
+  if (!slot_expert(slot, n_active, has_sh, E, expert_list, w13c, w13s, sh13c, sh13s, (size_t)2 * I * (H / 2),
+                   (size_t)2 * I * (H / 32), &C, &S)) {
+    // inactive slot past the list: nothing to do; bad id: contribute zeros
+    if (slot < n_active + (has_sh ? 1 : 0))
+      for (int i = threadIdx.x; i < 16 * T; i += 256) a_out[((size_t)slot * T + i / 16) * I + i0 + (i % 16)] = 0.f;
+    return;
+  }
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
+  for (int i = threadIdx.x; i < T * H; i += 256) xs[i] = x[i];
+  __syncthreads();
+  const uint32_t* xs32 = reinterpret_cast<const uint32_t*>(xs);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane >> 4, c = lane & 15;
+  const int NB = H / 32;
+  const size_t rowc = H / 2, rows = H / 32;
+
+  uint32_t xr[T == 1 ? NJ : 1][16];
+  if constexpr (T == 1) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int b = c + 16 * j;
+#pragma unroll
+      for (int d = 0; d < 16; ++d) xr[j][d] = (b < NB) ? xs32[b * 16 + d] : 0u;
+    }
+  }
+  // two steps of 4 rows: lanes 0-15 gate i, 16-31 gate i+1, 32-47 up i, 48-63 up i+1
+  uint4 cw[2][NJ];
+  uint32_t sb[2][NJ];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const int ri = i0 + 4 * wave + 2 * st + (r & 1);
+    const int row = (r < 2) ? ri : I + ri;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int b = c + 16 * j;
+      cw[st][j] = (b < NB) ? ld16(C + row * rowc + (size_t)b * 16) : make_uint4(0, 0, 0, 0);
+      sb[st][j] = (b < NB) ? (uint32_t)S[row * rows + b] : 127u;
+    }
+  }
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    float acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[t] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int b = c + 16 * j;
+      if (b >= NB) continue;
+      const float scale = e8m0_to_f32(sb[st][j]);
+      if constexpr (T == 1) {
+        acc[0] = fmaf(mx_block_dot(cw[st][j], xr[j]), scale, acc[0]);
+      } else {
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          uint32_t xp[16];
+          const uint4* src = reinterpret_cast<const uint4*>(xs32 + (size_t)t * (H / 2) + (size_t)b * 16);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uint4 v = src[q];
+            xp[4 * q] = v.x; xp[4 * q + 1] = v.y; xp[4 * q + 2] = v.z; xp[4 * q + 3] = v.w;
+          }
+          acc[t] = fmaf(mx_block_dot(cw[st][j], xp), scale, acc[t]);
+        }
+      }
+    }
+    const int ri = i0 + 4 * wave + 2 * st + (r & 1);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const float sum = sum16(acc[t]);
+      const float up = __shfl_xor(sum, 32);
+      if (r < 2 && c == 0) a_out[((size_t)slot * T + t) * I + ri] = silu(sum) * up;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- down + combine + residual
+
+template <int T, int NJD, bool ALDS>
+__global__ void __launch_bounds__(256) moe_down_kernel(int H, int I, int E, int max_slots,
+                                                       const uint8_t* __restrict__ w2c, const uint8_t* __restrict__ w2s,
+                                                       const uint8_t* __restrict__ sh2c, const uint8_t* __restrict__ sh2s,
+                                                       const int32_t* __restrict__ expert_list,
+                                                       const float* __restrict__ slot_w, const float* __restrict__ a_in,
+                                                       const uint16_t* __restrict__ residual, float* __restrict__ out_y,
+                                                       uint16_t* __restrict__ out_h, uint16_t* __restrict__ out_h2) {
+  int n_active = expert_list[0];
+  n_active = n_active < 0 ? 0 : (n_active > max_slots - 1 ? max_slots - 1 : n_active);
+  const bool has_sh = sh2c != nullptr;
+  const int nslots = n_active + (has_sh ? 1 : 0);
+  extern __shared__ __attribute__((aligned(16))) float as[];
+  if constexpr (ALDS) {
+    const int n = nslots * T * I;
+    const float4* src = reinterpret_cast<const float4*>(a_in);
+    float4* dst = reinterpret_cast<float4*>(as);
+    for (int i = threadIdx.x; i < n / 4; i += 256) dst[i] = src[i];
+    __syncthreads();
+  }
+  const float* A = ALDS ? as : a_in;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane >> 3, c = lane & 7;
+  const int n0 = blockIdx.x * 8;
+  const int row = n0 + r;
+  const int NBd = I / 32;
+  const size_t rowc = I / 2, rows = I / 32;
+
+  float acc[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) acc[t] = 0.f;
+  for (int s = wave; s < nslots; s += 4) {
+    const uint8_t *C, *S;
+    if (!slot_expert(s, n_active, has_sh, E, expert_list, w2c, w2s, sh2c, sh2s, (size_t)H * (I / 2),
+                     (size_t)H * (I / 32), &C, &S))
+      continue;
+    uint4 cw[NJD];
+    uint32_t sb[NJD];
+#pragma unroll
+    for (int j = 0; j < NJD; ++j) {
+      const int b = c + 8 * j;
+      cw[j] = (b < NBd) ? ld16(C + row * rowc + (size_t)b * 16) : make_uint4(0, 0, 0, 0);
+      sb[j] = (b < NBd) ? (uint32_t)S[row * rows + b] : 127u;
+    }
+    float wt[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) wt[t] = (s < n_active) ? slot_w[s * T + t] : 1.0f;
+#pragma unroll
+    for (int j = 0; j < NJD; ++j) {
+      const int b = c + 8 * j;
+      if (b >= NBd) continue;
+      const float scale = e8m0_to_f32(sb[j]);
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const float* ap = A + ((size_t)s * T + t) * I + (size_t)b * 32;
+        float av[32];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          float4 v = reinterpret_cast<const float4*>(ap)[q];
+          av[4 * q] = v.x; av[4 * q + 1] = v.y; av[4 * q + 2] = v.z; av[4 * q + 3] = v.w;
+        }
+        acc[t] = fmaf(wt[t] * scale, mx_block_dot_f32(cw[j], av), acc[t]);
+      }
+    }
+  }
+  __shared__ float part[4][8][T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const float v = sum8(acc[t]);
+    if (c == 0) part[wave][r][t] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < 8 * T) {
+    const int rr = threadIdx.x / T, t = threadIdx.x % T;
+    const float y = ((part[0][rr][t] + part[1][rr][t]) + part[2][rr][t]) + part[3][rr][t];
+    const size_t o = (size_t)t * H + n0 + rr;
+    if (out_y) out_y[o] = y;
+    if (residual) {
+      const uint16_t h = f32_to_bf16_rne(bf16_bits_to_f32(residual[o]) + y);
+      if (out_h) out_h[o] = h;
+      if (out_h2) out_h2[o] = h;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+
+bool experts_shape_supported(int H, int I) {
+  if (H % 32 || I % 32 || H > 8192 || I > 2048) return false;
+  const int nj = (H / 32 + 15) / 16, njd = (I / 32 + 7) / 8;
+  const bool ok_nj = nj == 1 || nj == 2 || nj == 4 || nj == 5 || nj == 8 || nj == 16;
+  const bool ok_njd = njd == 1 || njd == 2 || njd == 3 || njd == 4 || njd == 6 || njd == 8;
+  return ok_nj && ok_njd;
+}
+
+template <int T>
+static hipError_t launch_gateup_t(const uint16_t* x, int H, int I, int E, int max_slots, const uint8_t* w13c,
+                                  const uint8_t* w13s, const uint8_t* sh13c, const uint8_t* sh13s,
+                                  const int32_t* el, float* a, hipStream_t st) {
+  const int nj = (H / 32 + 15) / 16;
+  dim3 grid(I / 16, max_slots);
+  const size_t lds = (size_t)T * H * 2;
+#define WSX_G_CASE(N)                                                                                    \
+  case N:                                                                                                \
+    moe_gateup_kernel<T, N><<<grid, 256, lds, st>>>(x, H, I, E, max_slots, w13c, w13s, sh13c, sh13s, el, a); \
+    break;
+  switch (nj) {
+    WSX_G_CASE(1) WSX_G_CASE(2) WSX_G_CASE(4) WSX_G_CASE(5) WSX_G_CASE(8) WSX_G_CASE(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef WSX_G_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_gateup(const uint16_t* x, int T, int H, int I, int E, int k, const uint8_t* w13c,
+                         const uint8_t* w13s, const uint8_t* sh13c, const uint8_t* sh13s, const int32_t* el,
+                         float* a, hipStream_t st) {
+  const int max_slots = T * k + 1;
+  switch (T) {
+    case 1: return launch_gateup_t<1>(x, H, I, E, max_slots, w13c, w13s, sh13c, sh13s, el, a, st);
+    case 2: return launch_gateup_t<2>(x, H, I, E, max_slots, w13c, w13s, sh13c, sh13s, el, a, st);
+    case 3: return launch_gateup_t<3>(x, H, I, E, max_slots, w13c, w13s, sh13c, sh13s, el, a, st);
+    case 4: return launch_gateup_t<4>(x, H, I, E, max_slots, w13c, w13s, sh13c, sh13s, el, a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+constexpr size_t kDownLdsLimit = 64 * 1024;
+
+template <int T, bool ALDS>
+static hipError_t launch_down_t(int H, int I, int E, int max_slots, const uint8_t* w2c, const uint8_t* w2s,
+                                const uint8_t* sh2c, const uint8_t* sh2s, const int32_t* el, const float* sw,
+                                const float* a, const uint16_t* res, float* y, uint16_t* h, uint16_t* h2,
+                                hipStream_t st) {
+  const int njd = (I / 32 + 7) / 8;
+  const size_t lds = ALDS ? (size_t)max_slots * T * I * 4 : 0;
+#define WSX_D_CASE(N)                                                                                             \
+  case N:                                                                                                         \
+    moe_down_kernel<T, N, ALDS><<<H / 8, 256, lds, st>>>(H, I, E, max_slots, w2c, w2s, sh2c, sh2s, el, sw, a, res, \
+                                                          y, h, h2);                                               \
+    break;
+  switch (njd) {
+    WSX_D_CASE(1) WSX_D_CASE(2) WSX_D_CASE(3) WSX_D_CASE(4) WSX_D_CASE(6) WSX_D_CASE(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef WSX_D_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_down(int T, int H, int I, int E, int k, const uint8_t* w2c, const uint8_t* w2s,
+                       const uint8_t* sh2c, const uint8_t* sh2s, const int32_t* el, const float* sw, const float* a,
+                       const uint16_t* res, float* y, uint16_t* h, uint16_t* h2, hipStream_t st) {
+  const int max_slots = T * k + 1;
+  const bool alds = (size_t)max_slots * T * I * 4 <= kDownLdsLimit;
+#define WSX_DT(TV)                                                                                           \
+  case TV:                                                                                                   \
+    return alds ? launch_down_t<TV, true>(H, I, E, max_slots, w2c, w2s, sh2c, sh2s, el, sw, a, res, y, h, h2, st) \
+                : launch_down_t<TV, false>(H, I, E, max_slots, w2c, w2s, sh2c, sh2s, el, sw, a, res, y, h, h2, st);
+  switch (T) { WSX_DT(1) WSX_DT(2) WSX_DT(3) WSX_DT(4) }
+#undef WSX_DT
+  return hipErrorInvalidValue;
+}
+
+}  // namespace wsx

@@ -1,0 +1,195 @@
+// Device helpers for the gfx950 (CDNA4) decode-path kernels: number-format
+// conversions on the hardware converters, 128-bit block dot products and
+// wave64 reductions.  Internal header; not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wsx {
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- formats
+
+// E8M0 block scale byte -> 2^(b-127) as a binary32 (b = 0 is the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
+  return b ? __uint_as_float(b << 23) : __uint_as_float(0x00400000u);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// binary32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Two E2M1 codes (byte `sel` of w: low nibble = even element) -> two bf16, exact.
+template <int SEL>
+__device__ __forceinline__ bf16x2_t fp4x2_to_bf16x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL);
+}
+// Two E2M1 codes -> two fp32, exact.
+template <int SEL>
+__device__ __forceinline__ f32x2_t fp4x2_to_f32x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+}
+// Two E4M3FN codes (half `HI` of w: byte 2*HI is the first element) -> two bf16, exact.
+template <bool HI>
+__device__ __forceinline__ bf16x2_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+}
+
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2_t, w); }
+
+__device__ __forceinline__ float dot2(bf16x2_t a, bf16x2_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+}
+
+// ---------------------------------------------------------------- block dot products
+// Each takes one 16-byte granule of weights and the matching activations as
+// packed bf16 pairs, and returns the fp32 dot product (unscaled).
+
+// MXFP4: 32 E2M1 codes (one MX block) x 32 bf16 activations (16 dwords).
+__device__ __forceinline__ float mx_block_dot(uint4 c, const uint32_t* xp) {
+  float a0 = 0.f, a1 = 0.f;
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    a0 = dot2(fp4x2_to_bf16x2<0>(w[d]), as_bf16x2(xp[4 * d + 0]), a0);
+    a1 = dot2(fp4x2_to_bf16x2<1>(w[d]), as_bf16x2(xp[4 * d + 1]), a1);
+    a0 = dot2(fp4x2_to_bf16x2<2>(w[d]), as_bf16x2(xp[4 * d + 2]), a0);
+    a1 = dot2(fp4x2_to_bf16x2<3>(w[d]), as_bf16x2(xp[4 * d + 3]), a1);
+  }
+  return a0 + a1;
+}
+
+// E4M3FN: 16 codes x 16 bf16 activations (8 dwords).
+__device__ __forceinline__ float fp8_granule_dot(uint4 c, const uint32_t* xp) {
+  float a0 = 0.f, a1 = 0.f;
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    a0 = dot2(fp8x2_to_bf16x2<false>(w[d]), as_bf16x2(xp[2 * d + 0]), a0);
+    a1 = dot2(fp8x2_to_bf16x2<true>(w[d]), as_bf16x2(xp[2 * d + 1]), a1);
+  }
+  return a0 + a1;
+}
+
+// bf16: 8 weights x 8 bf16 activations (4 dwords).
+__device__ __forceinline__ float bf16_granule_dot(uint4 c, const uint32_t* xp) {
+  float a0 = dot2(as_bf16x2(c.x), as_bf16x2(xp[0]), 0.f);
+  float a1 = dot2(as_bf16x2(c.y), as_bf16x2(xp[1]), 0.f);
+  a0 = dot2(as_bf16x2(c.z), as_bf16x2(xp[2]), a0);
+  a1 = dot2(as_bf16x2(c.w), as_bf16x2(xp[3]), a1);
+  return a0 + a1;
+}
+
+// fp32: 4 weights x 4 bf16 activations (2 dwords), fp32 FMAs.
+__device__ __forceinline__ float f32_granule_dot(uint4 c, const uint32_t* xp) {
+  float a = __uint_as_float(c.x) * bf16_bits_to_f32(xp[0] & 0xFFFFu);
+  a = fmaf(__uint_as_float(c.y), bf16_bits_to_f32(xp[0] >> 16), a);
+  a = fmaf(__uint_as_float(c.z), bf16_bits_to_f32(xp[1] & 0xFFFFu), a);
+  a = fmaf(__uint_as_float(c.w), bf16_bits_to_f32(xp[1] >> 16), a);
+  return a;
+}
+
+// ---------------------------------------------------------------- cross-lane reductions
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// DPP controls (gfx9 encoding)
+constexpr int kQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+// Sum over each aligned group of 8 lanes; every lane of the group gets the sum.
+// The addition tree is the same for every group and every lane.
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp_f<kQuadSwap1>(v);
+  v += dpp_f<kQuadSwap2>(v);
+  v += dpp_f<kRowHalfMirror>(v);
+  return v;
+}
+// Sum over each 16-lane DPP row.
+__device__ __forceinline__ float sum16(float v) {
+  v = sum8(v);
+  v += dpp_f<kRowMirror>(v);
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v = sum16(v);
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// (value, index) argmax over the wave: larger value wins, equal values go to
+// the lower index.  Every lane returns the winner.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    float ov = __shfl_xor(v, o);
+    int oi = __shfl_xor(i, o);
+    if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+  }
+}
+
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+// ---------------------------------------------------------------- memory
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Device-coherent accesses for data exchanged between workgroups inside one
+// launch.  Agent-scope relaxed atomics are performed at the device coherence
+// point (they bypass the per-XCD L2 for coherence), so no cache-wide
+// writeback or invalidate is needed: a store is visible device-wide once it
+// has been acknowledged (vmcnt), and such a load never returns a stale line.
+__device__ __forceinline__ void st_dev(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ void st_dev(int* p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ float ld_dev(const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ int ld_dev(const int* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+// Last-arriver election.  Every workgroup calls this once, after publishing its
+// partial results with st_dev; exactly one workgroup (the last to arrive) gets
+// true, and may then read every partial with ld_dev.  The workgroup-scope
+// release makes each thread wait until its own device-scope stores are
+// acknowledged; the barrier then covers the whole workgroup before the
+// counter increment.  The winner returns the counter to zero, so it is
+// reusable by the next launch without clearing.
+__device__ __forceinline__ bool last_block_arrived(unsigned* counter, unsigned nblocks, int* smem_flag) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *smem_flag = (old == nblocks - 1);
+    if (old == nblocks - 1) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  return *smem_flag != 0;
+}
+
+}  // namespace wsx
