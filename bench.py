@@ -71,19 +71,23 @@ def main():
     router = torch.empty((L, E, H), dtype=torch.bfloat16, device=dev)
     sh = [torch.empty((L,) + s[2:], dtype=torch.uint8, device=dev) for s in
           (shapes["w13c"], shapes["w13s"], shapes["w2c"], shapes["w2s"])]
+    # one pinned host staging buffer per tensor, refilled for every layer (first-touch of
+    # fresh host memory costs more than generating the bytes)
+    stage_t = {key: torch.empty(s[1:], dtype=torch.uint8, pin_memory=True) for key, s in shapes.items()}
+    stage = {key: t.numpy() for key, t in stage_t.items()}
     host_layer0 = None
     for l in range(L):
-        lw = inputs.layer_weights(wl, l)
+        lw = inputs.layer_weights(wl, l, out=stage)
         for key in shapes:
-            dw[key][l].copy_(torch.from_numpy(lw[key]))
+            dw[key][l].copy_(stage_t[key])
         router[l].copy_(torch.from_numpy(lw["router"].view(np.int16)).view(torch.bfloat16))
         for i in range(4):
             sh[i][l].copy_(torch.from_numpy(lw["shared"][i]))
         if l == 0:
-            host_layer0 = lw
-        del lw
-        if l % 8 == 7:
+            host_layer0 = {key: v.copy() if isinstance(v, np.ndarray) else v for key, v in lw.items()}
+        if l % 4 == 3:
             log(f"generated {l + 1}/{L} layers ({time.time() - t0:.0f} s)")
+    del stage, stage_t
     stack = ops.MoeStackTensors(router, dw["w13c"], dw["w13s"], dw["w2c"], dw["w2s"], shared=tuple(sh), k=k)
     resident = sum(t.numel() * t.element_size() for t in list(dw.values()) + sh + [router])
     head_w_host = inputs.head_weights(configs.LM_HEAD)

@@ -95,3 +95,57 @@ def test_decode_step_is_deterministic(ops, ling_stack):
     for _ in range(10):
         b = ops.moe_decode_step(h0, stack, head)
         assert torch.equal(a["h"], b["h"]) and torch.equal(a["logits"], b["logits"])
+
+
+def test_fused_step_many_consecutive_calls(ops, ling_stack):
+    """The single-launch step keeps a per-workspace epoch; consecutive calls on
+    one workspace (with and without traces, plain and captured in a graph) must
+    all complete without a failed wait and give identical results for
+    identical inputs."""
+    wl, layers, stack, head, qh, sh = ling_stack
+    H = wl.moe.H
+    ws = ops.workspace(ops.decode_step_workspace_bytes(1, H, wl.moe.I, wl.moe.E, wl.moe.k, head.V), "cuda")
+    xs = [P.to_dev_bf16(inputs.normal_bf16((wl.seed, 77, s), (1, H), 1.0)) for s in range(3)]
+    first = [ops.moe_decode_step(x, stack, head, ws=ws) for x in xs]
+    torch.cuda.synchronize()
+    for o in first:
+        assert int(o["argmax"][0]) >= 0
+    for rep in range(20):
+        for x, f in zip(xs, first):
+            o = ops.moe_decode_step(x, stack, head, ws=ws, trace=(rep % 5 == 0))
+            assert torch.equal(o["h"], f["h"]) and torch.equal(o["logits"], f["logits"])
+            assert torch.equal(o["argmax"], f["argmax"])
+    # replayed from a captured graph, with eager work between replays
+    h_in = torch.empty_like(xs[0])
+    out = dict(h=torch.empty_like(xs[0]), logits=torch.empty_like(first[0]["logits"]),
+               argmax=torch.empty_like(first[0]["argmax"]))
+    h_in.copy_(xs[0])
+    ops.moe_decode_step(h_in, stack, head, ws=ws, out=out)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ops.moe_decode_step(h_in, stack, head, ws=ws, out=out)
+    for rep in range(6):
+        i = rep % 3
+        h_in.copy_(xs[i])
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out["argmax"], first[i]["argmax"]) and torch.equal(out["h"], first[i]["h"])
+        assert torch.equal(out["logits"], first[i]["logits"])
+        ops.moe_decode_step(xs[(i + 1) % 3], stack, head, ws=ws)     # eager call between replays
+
+
+def test_same_workspace_decode_and_verify_passes(ops):
+    """One workspace serves 1-token steps (single launch) and 4-token verify
+    passes (per-phase launches) alternately."""
+    wl = configs.TINY
+    layers, stack = build_stack(ops, wl, 2)
+    head = ops.Fp8LmHead.quantize(P.to_dev_bf16(inputs.head_weights(wl, K=wl.moe.H)))
+    qh, sh = P.np_(head.q), P.np_(head.s)
+    H = wl.moe.H
+    ws = ops.workspace(ops.decode_step_workspace_bytes(4, H, wl.moe.I, wl.moe.E, wl.moe.k, head.V), "cuda")
+    for step in range(4):
+        T = 1 if step % 2 == 0 else 4
+        h0 = inputs.normal_bf16((wl.seed, 55, step), (T, H), 1.0)
+        out = ops.moe_decode_step(P.to_dev_bf16(h0), stack, head, trace=True, ws=ws)
+        check_step(wl, layers, out, qh, sh, h0)

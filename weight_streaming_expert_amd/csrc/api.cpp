@@ -104,9 +104,9 @@ size_t wsx_lm_head_workspace_bytes(int T, int V, int K) {
 }
 
 size_t wsx_decode_step_workspace_bytes(int T, int H, int I, int E, int k, int V) {
-  (void)V;
-  if (T < 1 || T > WSX_MAX_T || k < 1 || k > WSX_MAX_K || E < 1 || E > WSX_MAX_E || I < 0 || H < 0) return 0;
-  return step_ws(T, H, I, E, k).total;
+  if (T < 1 || T > WSX_MAX_T || k < 1 || k > WSX_MAX_K || E < 1 || E > WSX_MAX_E || I < 0 || H < 0 || V < 0) return 0;
+  // the single-launch step's exchange buffers, then the per-phase region
+  return fused_step_workspace_bytes(H, I, E, k, V) + step_ws(T, H, I, E, k).total;
 }
 
 wsx_status moe_route_topk(const uint16_t* x, const void* w_router, int router_dtype, int T, int H, int E, int k,
@@ -178,6 +178,7 @@ wsx_status moe_decode_step(const uint16_t* h_in, int T, const wsx_moe_stack* sk,
                            size_t ws_bytes, void* stream) {
   if (!sk || !h_in || !head_q || !head_scale || !h_out || !argmax) return WSX_ERR_NULL;
   if (sk->L < 1) return WSX_ERR_SHAPE;
+  if (sk->L > WSX_MAX_LAYERS - 1) return WSX_ERR_UNSUPPORTED;
   const int H = sk->H, I = sk->I, E = sk->E, k = sk->k, L = sk->L;
   wsx_status st = check_router(h_in, sk->w_router, sk->router_dtype, T, H, E, k);
   if (st != WSX_OK) return st;
@@ -189,9 +190,15 @@ wsx_status moe_decode_step(const uint16_t* h_in, int T, const wsx_moe_stack* sk,
   if (!a16(head_q) || !a16(h_out)) return WSX_ERR_ALIGN;
   if ((h_trace && !a16(h_trace)) || (u_trace && !a16(u_trace))) return WSX_ERR_ALIGN;
   const StepWs W = step_ws(T, H, I, E, k);
-  if ((st = check_ws(ws, ws_bytes, W.total)) != WSX_OK) return st;
+  // workspace: the single-launch step's exchange buffers first (their place
+  // does not depend on T), then the per-phase region
+  const size_t fused_bytes = fused_step_workspace_bytes(H, I, E, k, V);
+  if ((st = check_ws(ws, ws_bytes, fused_bytes + W.total)) != WSX_OK) return st;
+  if (fused_step_supported(T, sk->router_dtype, sk->sh13_codes != nullptr, H, I, E, k))
+    return hip_status(launch_fused_step(sk, h_in, head_q, head_scale, V, h_out, logits, argmax, h_trace, u_trace,
+                                        ids_trace, w_trace, ws, S(stream), kStepSegments));
 
-  char* base = reinterpret_cast<char*>(ws);
+  char* base = reinterpret_cast<char*>(ws) + fused_bytes;
   unsigned* counter = reinterpret_cast<unsigned*>(base + W.moe.counter);
   float* rlogits = reinterpret_cast<float*>(base + W.moe.logits);
   float* a = reinterpret_cast<float*>(base + W.moe.a);

@@ -1,0 +1,1164 @@
+// One decode step (T = 1) of the stacked MoE layers plus the FP8 LM head in a
+// single launch on gfx950.
+//
+// [saipien] "Why one user waits on weights": at batch size 1 the step is a
+// stream of weight reads (8 of 512 routed experts plus the shared expert per
+// layer, then the 157,184-row vocabulary projection); [saipien] "Stop hauling
+// the vocabulary in full precision" for the FP8 head; [ncij] "What happens on
+// a real workload?" for greedy decoding.
+//
+// Why one launch: a kernel boundary in a captured graph costs ~1.7 us on
+// MI355X and a layer has three all-to-all dependencies (the full residual
+// stream before the router, all router logits before the top-k, all expert
+// activations before the down projection), so per-kernel phases would pay
+// ~100 boundaries per step.  Here every phase of every layer is a set of
+// workgroups of one grid, in dependency order:
+//
+//   per layer l:  R (router rows)  S (shared gate/up tiles)  G (routed gate/up
+//                 tiles, k slots)  D (down rows over all slots, + residual)
+//   then:         head rows and a two-level argmax
+//
+// A workgroup only ever waits for data produced by workgroups with a LOWER
+// index.  Workgroups are dispatched in index order, so the lowest-indexed
+// unfinished workgroup never waits for anything unfinished, and the grid
+// always drains.  Every wait is also bounded: on timeout it raises an error
+// word, all later waits return at once and the step reports argmax = -1.
+//
+// Data crosses workgroups only through device-coherent (sc1) stores and loads,
+// performed at the device coherence point, and every exchanged value travels
+// with a tag (step and layer) in the same 8-byte store, so a reader that sees
+// the tag sees the value and no cache-wide fence is needed.  The exchange
+// buffers are reused from layer to layer: a layer only overwrites them after
+// every reader of the previous layer has provably finished (each such reader
+// is an ancestor of the data the writer waited for).  Weights that do not
+// depend on routing (the router rows, the shared expert, the first head rows)
+// are loaded BEFORE a workgroup starts waiting, so their HBM reads overlap the
+// earlier phases.  A workgroup that is dispatched long before its inputs can
+// exist first sleeps on one word of the stage before (cheap), and only then
+// polls its whole input.
+#include "wsx_device.h"
+#include "wsx_internal.h"
+
+namespace wsx {
+
+namespace {
+
+constexpr int NT = 256;            // threads per workgroup
+constexpr int kRRows = 8;          // router rows per R workgroup
+constexpr int kGRows = 16;         // intermediate values per S/G workgroup
+constexpr int kDRows = 8;          // output rows per D workgroup
+constexpr int kHeadGroup = 32;     // head workgroups per first-level argmax group
+constexpr int kSpinMax = 1 << 17;  // polls before a wait gives up
+constexpr unsigned kEpochMod = (1u << 24) - 1;   // epochs cycle in [0, kEpochMod)
+// Copies of each exchange buffer: every consumer polls the copy picked by its
+// workgroup index, so no single cache line is hammered by hundreds of pollers.
+constexpr int kCopiesH = 8;        // residual stream
+constexpr int kCopiesLg = 16;      // router logits
+constexpr int kCopiesA = 8;        // expert activations
+constexpr unsigned kHeadTag = 255;               // layer field of the head's tags
+
+struct Ctl {   // control words, each on its own 256-byte line
+  unsigned epoch;
+  unsigned pad0[63];
+  unsigned err;
+  unsigned pad1[63];
+  unsigned top_counter;
+  unsigned pad2[63];
+};
+
+}  // namespace
+
+struct FusedBufs {
+  void* ctl;                 // Ctl
+  unsigned* group_counter;   // [n_groups], 64-byte stride
+  uint2* hx;                 // [kCopiesH][2][H/2] (bf16 pair, tag); h_l lives in [.][l & 1] (l >= 1)
+  uint2* ssx;                // [kCopiesH][2][H/8] (sum of squares of 8 rows of h_l, tag), beside hx
+  uint2* lg;                 // [kCopiesLg][E] (logit, tag) of the current layer
+  uint2* a;                  // [kCopiesA][nslot][I] (activation, tag) of the current layer
+  uint4* hpart;              // [n_head] (value, index, tag, -)
+  uint4* gpart;              // [n_groups]
+};
+
+struct FusedStepArgs {
+  const void* router;
+  const uint8_t *w13c, *w13s, *w2c, *w2s;
+  const uint8_t *sh13c, *sh13s, *sh2c, *sh2s;
+  const uint8_t* hq;
+  const float* hs;
+  const uint16_t* h_in;
+  uint16_t* h_out;
+  float* logits;
+  int32_t* argmax;
+  uint16_t* h_trace;
+  uint16_t* u_trace;
+  int32_t* ids_trace;
+  float* w_trace;
+  FusedBufs b;
+  int L, H, I, E, k, V;
+  int nslot, nR, nS, nG, nD, per_layer, n_head, n_groups;
+  int block0;   // index of this launch's first workgroup in the step's workgroup order
+};
+
+namespace {
+
+__device__ __forceinline__ Ctl* ctl(const FusedStepArgs& A) { return reinterpret_cast<Ctl*>(A.b.ctl); }
+__device__ __forceinline__ void raise_err(const FusedStepArgs& A) { st_dev(reinterpret_cast<int*>(&ctl(A)->err), 1); }
+__device__ __forceinline__ bool err_set(const FusedStepArgs& A) {
+  return ld_dev(reinterpret_cast<const int*>(&ctl(A)->err)) != 0;
+}
+
+// LDS layouts of the normalized activations, chosen so that the 8 lanes a
+// 16-byte LDS read serves at once hit disjoint banks:
+//   LayPlain  element i at i (router rows: lanes read consecutive 16-byte granules)
+//   LayMX     32-element MX blocks at an 80-byte stride (gate/up: lane c reads block c)
+//   LayHead   16-element FP8 granules at a 48-byte stride (head: lane c reads granule c)
+struct LayPlain {
+  static __device__ __forceinline__ int pos(int i) { return i; }
+  static constexpr int bytes(int H) { return H * 2; }
+};
+struct LayMX {
+  static __device__ __forceinline__ int pos(int i) { return (i >> 5) * 40 + (i & 31); }
+  static constexpr int bytes(int H) { return H / 32 * 80; }
+};
+struct LayHead {
+  static __device__ __forceinline__ int pos(int i) { return (i >> 4) * 24 + (i & 15); }
+  static constexpr int bytes(int H) { return H / 16 * 48; }
+};
+// Expert activations in LDS: per slot, 32-value blocks at a 144-byte stride.
+__device__ __forceinline__ int apos(int s, int i, int I) { return s * (I / 32) * 36 + (i >> 5) * 36 + (i & 31); }
+
+__device__ __forceinline__ uint2* hx_buf(const FusedStepArgs& A, int l, int c) {
+  return A.b.hx + ((size_t)c * 2 + (l & 1)) * (A.H / 2);
+}
+__device__ __forceinline__ uint2* ss_buf(const FusedStepArgs& A, int l, int c) {
+  return A.b.ssx + ((size_t)c * 2 + (l & 1)) * (A.H / kDRows);
+}
+__device__ __forceinline__ uint2* lg_buf(const FusedStepArgs& A, int c) { return A.b.lg + (size_t)c * A.E; }
+__device__ __forceinline__ uint2* a_buf(const FusedStepArgs& A, int c) { return A.b.a + (size_t)c * A.nslot * A.I; }
+__device__ __forceinline__ int my_copy(int copies) { return (int)(blockIdx.x % copies); }
+
+// ---------------------------------------------------------------- waits
+
+// Whole-workgroup decision to stop waiting: the wait has run too long, or
+// another wait already failed.  Thread 0 decides for everyone.
+__device__ __forceinline__ bool block_should_bail(const FusedStepArgs& A, int it) {
+  int bail = 0;
+  if (threadIdx.x == 0) {
+    if (it >= kSpinMax) { raise_err(A); bail = 1; }
+    else if ((it & 15) == 15 && err_set(A)) bail = 1;
+  }
+  return __syncthreads_or(bail) != 0;
+}
+
+// The same for one wavefront (lane 0 decides).
+__device__ __forceinline__ bool wave_should_bail(const FusedStepArgs& A, int it) {
+  int bail = 0;
+  if ((threadIdx.x & 63) == 0) {
+    if (it >= kSpinMax) { raise_err(A); bail = 1; }
+    else if ((it & 15) == 15 && err_set(A)) bail = 1;
+  }
+  return __shfl(bail, 0) != 0;
+}
+
+// Sleep on the tag of one exchanged (value, tag) pair until it equals `want`.
+// Used to wait cheaply for the stage before the one a workgroup needs; gives
+// up quietly, since the full poll that follows has its own bound.
+__device__ __forceinline__ void sleep_on_tag(const FusedStepArgs& A, const uint2* p, int index, unsigned want) {
+  for (int it = 0; it < kSpinMax; ++it) {
+    if (ld_coh4(p, (uint32_t)index * 8 + 4) == want) return;
+    if ((it & 15) == 15 && err_set(A)) return;
+    __builtin_amdgcn_s_sleep(8);
+  }
+}
+
+// Each wavefront derives the RMS scale r = 1/sqrt(mean(h^2) + 1e-6) itself
+// from the published per-tile sums of squares (SPL 16-byte chunks of two
+// partials per lane, chunk q = lane + 64 i), summed in one fixed order, so
+// every wavefront of every workgroup gets bit-identical r.
+template <int SPL>
+__device__ __forceinline__ float wave_rscale(const uint4 (&sp)[SPL], int H) {
+  float ps = 0.f;
+#pragma unroll
+  for (int i = 0; i < SPL; ++i) ps += __uint_as_float(sp[i].x) + __uint_as_float(sp[i].z);
+  const float total = wave_sum_dpp(ps);
+  return 1.0f / sqrtf(total / (float)H + 1e-6f);
+}
+
+// u_l = RNE_bf16(h_l * r) into LDS (layout Lay), once every pair of h_l and
+// every partial sum of squares carries `tag`.  Each wavefront polls its share
+// of h (QPT 16-byte chunks per lane, chunk q = thread + 256 i) and all the
+// partials, without workgroup barriers; one barrier follows.
+template <int QPT, int SPL, class Lay>
+__device__ __forceinline__ void wait_u(const FusedStepArgs& A, int l, unsigned tag, uint16_t* xs) {
+  const int lane = threadIdx.x & 63;
+  const int nq = A.H / 4, nsq = A.H / kDRows / 2;
+  const uint2* hxl = hx_buf(A, l, my_copy(kCopiesH));
+  const uint2* ssl = ss_buf(A, l, my_copy(kCopiesH));
+  uint4 v[QPT], sp[SPL];
+  for (int it = 0;; ++it) {
+    int ok = 1;
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int q = threadIdx.x + NT * i;
+      v[i] = make_uint4(0, 0, 0, 0);
+      if (q < nq) {
+        v[i] = ld_coh16(hxl, (uint32_t)q * 16);
+        ok &= (v[i].y == tag) & (v[i].w == tag);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+      const int q = lane + 64 * i;
+      sp[i] = make_uint4(0, 0, 0, 0);
+      if (q < nsq) {
+        sp[i] = ld_coh16(ssl, (uint32_t)q * 16);
+        ok &= (sp[i].y == tag) & (sp[i].w == tag);
+      }
+    }
+    if (__all(ok)) break;
+    if (wave_should_bail(A, it)) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  const float r = wave_rscale<SPL>(sp, A.H);
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int q = threadIdx.x + NT * i;
+    if (q < nq) {
+      const uint32_t a = f32_to_bf16_rne(bf16_bits_to_f32(v[i].x & 0xFFFFu) * r);
+      const uint32_t b = f32_to_bf16_rne(bf16_bits_to_f32(v[i].x >> 16) * r);
+      const uint32_t c = f32_to_bf16_rne(bf16_bits_to_f32(v[i].z & 0xFFFFu) * r);
+      const uint32_t d = f32_to_bf16_rne(bf16_bits_to_f32(v[i].z >> 16) * r);
+      *reinterpret_cast<uint2*>(xs + Lay::pos(4 * q)) = make_uint2(a | (b << 16), c | (d << 16));
+    }
+  }
+  __syncthreads();
+}
+
+// The kernel's input residual stream -> LDS (layout Lay), 8 elements per chunk.
+template <class Lay>
+__device__ __forceinline__ void load_h_input(const uint16_t* h, int H, uint16_t* xs) {
+  uint4 v[3];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int q = threadIdx.x + NT * i;
+    v[i] = make_uint4(0, 0, 0, 0);
+    if (q < H / 8) v[i] = ld16(h + (size_t)q * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int q = threadIdx.x + NT * i;
+    if (q < H / 8) *reinterpret_cast<uint4*>(xs + Lay::pos(8 * q)) = v[i];
+  }
+  for (int q = threadIdx.x + 3 * NT; q < H / 8; q += NT)
+    *reinterpret_cast<uint4*>(xs + Lay::pos(8 * q)) = ld16(h + (size_t)q * 8);
+  __syncthreads();
+}
+
+template <class Lay>
+__device__ __forceinline__ void rms_norm_inplace(uint16_t* xs, int H, float* red);
+
+// u_l for layer l into LDS: from the kernel input (with a workgroup reduction
+// for the scale) for l = 0, else from the tagged stream and its partials.
+template <int QPT, int SPL, class Lay>
+__device__ __forceinline__ void get_u(const FusedStepArgs& A, int l, unsigned base, uint16_t* xs, float* red) {
+  if (l == 0) {
+    load_h_input<Lay>(A.h_in, A.H, xs);
+    rms_norm_inplace<Lay>(xs, A.H, red);
+  } else {
+    wait_u<QPT, SPL, Lay>(A, l, base + l - 1, xs);
+  }
+}
+
+// The same when h_l is known to be complete already: the loads are issued
+// now (before the caller's weight loads, so their data arrives first) and
+// committed to LDS later; a tag mismatch can only mean a broken step and
+// raises the error word.
+template <int QPT, int SPL>
+struct HRegs {
+  uint4 v[QPT];
+  uint4 sp[SPL];
+};
+
+template <int QPT, int SPL>
+__device__ __forceinline__ void h_issue(const FusedStepArgs& A, int l, HRegs<QPT, SPL>& r) {
+  const int lane = threadIdx.x & 63;
+  const uint2* src = hx_buf(A, l, my_copy(kCopiesH));
+  const uint2* ssl = ss_buf(A, l, my_copy(kCopiesH));
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int q = threadIdx.x + NT * i;
+    r.v[i] = make_uint4(0, 0, 0, 0);
+    if (l == 0) {
+      if (q < A.H / 8) r.v[i] = ld16(A.h_in + (size_t)q * 8);
+    } else {
+      if (q < A.H / 4) r.v[i] = ld_coh16(src, (uint32_t)q * 16);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < SPL; ++i) {
+    const int q = lane + 64 * i;
+    r.sp[i] = make_uint4(0, 0, 0, 0);
+    if (l > 0 && q < A.H / kDRows / 2) r.sp[i] = ld_coh16(ssl, (uint32_t)q * 16);
+  }
+}
+
+// Commits the loads of h_issue as u_l in LDS (layout Lay).
+template <int QPT, int SPL, class Lay>
+__device__ __forceinline__ void h_commit(const FusedStepArgs& A, int l, unsigned base, const HRegs<QPT, SPL>& r,
+                                         uint16_t* xs, float* red) {
+  if (l == 0) {
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int q = threadIdx.x + NT * i;
+      if (q < A.H / 8) *reinterpret_cast<uint4*>(xs + Lay::pos(8 * q)) = r.v[i];
+    }
+    __syncthreads();
+    rms_norm_inplace<Lay>(xs, A.H, red);
+    return;
+  }
+  const int lane = threadIdx.x & 63;
+  const unsigned tag = base + l - 1;
+  int bad = 0;
+#pragma unroll
+  for (int i = 0; i < SPL; ++i)
+    if (lane + 64 * i < A.H / kDRows / 2) bad |= (r.sp[i].y != tag) | (r.sp[i].w != tag);
+  const float sc = wave_rscale<SPL>(r.sp, A.H);
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int q = threadIdx.x + NT * i;
+    if (q < A.H / 4) {
+      bad |= (r.v[i].y != tag) | (r.v[i].w != tag);
+      const uint32_t a = f32_to_bf16_rne(bf16_bits_to_f32(r.v[i].x & 0xFFFFu) * sc);
+      const uint32_t b = f32_to_bf16_rne(bf16_bits_to_f32(r.v[i].x >> 16) * sc);
+      const uint32_t c = f32_to_bf16_rne(bf16_bits_to_f32(r.v[i].z & 0xFFFFu) * sc);
+      const uint32_t d = f32_to_bf16_rne(bf16_bits_to_f32(r.v[i].z >> 16) * sc);
+      *reinterpret_cast<uint2*>(xs + Lay::pos(4 * q)) = make_uint2(a | (b << 16), c | (d << 16));
+    }
+  }
+  if (bad) raise_err(A);
+  __syncthreads();
+}
+
+// u = RNE_bf16(h / sqrt(mean(h^2) + 1e-6)) in place.  The sum of squares has
+// one fixed order in every workgroup that calls this, so all of them derive
+// bit-identical u.
+template <class Lay>
+__device__ __forceinline__ void rms_norm_inplace(uint16_t* xs, int H, float* red) {
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < H; i += NT) {
+    const float v = bf16_bits_to_f32(xs[Lay::pos(i)]);
+    ss = fmaf(v, v, ss);
+  }
+  ss = wave_sum_dpp(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float s = ((red[0] + red[1]) + red[2]) + red[3];
+  const float r = 1.0f / sqrtf(s / (float)H + 1e-6f);
+  for (int i = threadIdx.x; i < H; i += NT) xs[Lay::pos(i)] = f32_to_bf16_rne(bf16_bits_to_f32(xs[Lay::pos(i)]) * r);
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- routing
+
+struct Routing {
+  int rid[WSX_MAX_K];      // selected ids in rank order
+  float rw[WSX_MAX_K];     // routing weights in rank order
+  int sid[WSX_MAX_K];      // selected ids, ascending (slot order)
+  float sw[WSX_MAX_K];     // routing weight of each slot
+};
+
+// Afterwards (va, ia) ranks before (vb, ib): larger value, then lower id.
+__device__ __forceinline__ void cmpswap(float& va, int& ia, float& vb, int& ib) {
+  if (better(vb, ib, va, ia)) {
+    const float tv = va; va = vb; vb = tv;
+    const int ti = ia; ia = ib; ib = ti;
+  }
+}
+
+// Top-k routing of one layer: wavefront 0 waits until the E logits carry
+// `tag` (lane L holds logits L*EPL .. L*EPL+EPL-1), sorts its EPL values, then
+// takes k rounds of a DPP wavefront maximum over the lanes' heads (equal
+// maxima go to the lowest lane, whose ids are the lowest, and within a lane
+// the sort keeps ids ascending).  The selected logits, the softmax over them
+// and the ascending slot order are all computed on wavefront-uniform values
+// in registers; the result is left in LDS for the whole workgroup.
+template <int EPL>
+__device__ __forceinline__ void block_route(const FusedStepArgs& A, unsigned tag, Routing* R) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int E = A.E, k = A.k;
+    const int e0 = lane * EPL;
+    const uint2* lgc = lg_buf(A, my_copy(kCopiesLg));
+    float v[EPL];
+    int id[EPL];
+    for (int it = 0;; ++it) {
+      int ok = 1;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        id[i] = e0 + i < E ? e0 + i : 0x7FFFFFFF;
+        v[i] = -INFINITY;
+      }
+      if constexpr (EPL % 2 == 0) {
+#pragma unroll
+        for (int i = 0; i < EPL; i += 2) {
+          if (e0 + i < E) {
+            const uint4 q = ld_coh16(lgc, (uint32_t)(e0 + i) * 8);
+            v[i] = __uint_as_float(q.x);
+            v[i + 1] = __uint_as_float(q.z);
+            ok &= (q.y == tag) & (q.w == tag);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+          if (e0 + i < E) {
+            const uint2 q = ld_coh8(lgc, (uint32_t)(e0 + i) * 8);
+            v[i] = __uint_as_float(q.x);
+            ok &= (q.y == tag);
+          }
+        }
+      }
+      if (__all(ok)) break;
+      if (wave_should_bail(A, it)) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    // lane-local sort (fixed network over compile-time indices)
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+#pragma unroll
+      for (int j = 0; j < EPL - 1 - i; ++j) cmpswap(v[j], id[j], v[j + 1], id[j + 1]);
+    float top[WSX_MAX_K];
+    int topi[WSX_MAX_K];
+#pragma unroll
+    for (int j = 0; j < WSX_MAX_K; ++j) {
+      top[j] = -INFINITY;
+      topi[j] = 0x7FFFFFFF;
+      if (j < k) {
+        const float m = wave_max_dpp(v[0]);
+        const unsigned long long owners = __ballot(v[0] == m);
+        const int owner = __ffsll((long long)owners) - 1;
+        top[j] = m;
+        topi[j] = __builtin_amdgcn_readlane(id[0], owner);
+        if (lane == owner) {
+#pragma unroll
+          for (int i = 0; i < EPL - 1; ++i) { v[i] = v[i + 1]; id[i] = id[i + 1]; }
+          v[EPL - 1] = -INFINITY;
+          id[EPL - 1] = 0x7FFFFFFF;
+        }
+      }
+    }
+    // softmax over the selected logits, in rank order
+    float z[WSX_MAX_K], zs = 0.f;
+#pragma unroll
+    for (int j = 0; j < WSX_MAX_K; ++j) {
+      z[j] = 0.f;
+      if (j < k) { z[j] = __expf(top[j] - top[0]); zs += z[j]; }
+    }
+    if (lane < k) {
+      int myid = 0, slot = 0;
+      float myw = 0.f;
+#pragma unroll
+      for (int j = 0; j < WSX_MAX_K; ++j)
+        if (j == lane) { myid = topi[j]; myw = z[j] / zs; }
+#pragma unroll
+      for (int j = 0; j < WSX_MAX_K; ++j) slot += (j < k) & (topi[j] < myid);
+      R->rid[lane] = myid;
+      R->rw[lane] = myw;
+      R->sid[slot] = myid;
+      R->sw[slot] = myw;
+    }
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- gate/up tile
+
+// Rows of one expert's [2I][H] gate/up matrix for the intermediate values
+// i0 .. i0+15: wavefront w, step st covers gate rows i0+4w+2st+{0,1} (lanes
+// 0-15, 16-31) and the matching up rows (lanes 32-47, 48-63); 16 lanes per
+// row, lane c takes MX blocks c, c+16, ...
+template <int NJ>
+struct GateUpRegs {
+  uint4 cw[2][NJ];
+  uint32_t sb[2][NJ];
+};
+
+template <int NJ>
+__device__ __forceinline__ void gateup_load(const uint8_t* C, const uint8_t* S, int H, int I, int i0,
+                                            GateUpRegs<NJ>& g) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane >> 4, c = lane & 15;
+  const int NB = H / 32;
+  const size_t rowc = H / 2, rows = H / 32;
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const int ri = i0 + 4 * wave + 2 * st + (r & 1);
+    const int row = (r < 2) ? ri : I + ri;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int b = c + 16 * j;
+      g.cw[st][j] = (b < NB) ? ld16(C + row * rowc + (size_t)b * 16) : make_uint4(0, 0, 0, 0);
+      g.sb[st][j] = (b < NB) ? (uint32_t)S[row * rows + b] : 127u;
+    }
+  }
+}
+
+// a = silu(Wg u) * (Wu u) for the 16 values of the tile, stored as tagged
+// pairs at a_slot[i].
+template <int NJ>
+__device__ __forceinline__ void gateup_compute(const GateUpRegs<NJ>& g, const uint32_t* xs32, int H, int i0,
+                                               uint2* a_slot, size_t a_copy_stride, unsigned tag) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane >> 4, c = lane & 15;
+  const int NB = H / 32;
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int b = c + 16 * j;
+      if (b < NB) {
+        uint32_t xp[16];
+        const uint4* src = reinterpret_cast<const uint4*>(xs32 + b * 20);   // LayMX: 80-byte blocks
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint4 t = src[q];
+          xp[4 * q] = t.x; xp[4 * q + 1] = t.y; xp[4 * q + 2] = t.z; xp[4 * q + 3] = t.w;
+        }
+        acc = fmaf(mx_block_dot(g.cw[st][j], xp), e8m0_to_f32(g.sb[st][j]), acc);
+      }
+    }
+    const float sum = sum16(acc);
+    const float up = __shfl_xor(sum, 32);
+    const int ri = i0 + 4 * wave + 2 * st + (r & 1);
+    // lanes c < kCopiesA of the two gate rows each publish one copy
+    if (r < 2 && c < kCopiesA)
+      st_coh8(a_slot + (size_t)c * a_copy_stride, (uint32_t)ri * 8, make_uint2(__float_as_uint(silu(sum) * up), tag));
+  }
+}
+
+// ---------------------------------------------------------------- down tile
+
+// Rows n0 .. n0+7 of one expert's [H][I] down matrix: 8 lanes per row, lane c
+// takes MX blocks c, c+8, ...
+template <int NJD>
+struct DownRegs {
+  uint4 cw[NJD];
+  uint32_t sb[NJD];
+};
+
+template <int NJD>
+__device__ __forceinline__ void down_load(const uint8_t* C, const uint8_t* S, int I, int n0, DownRegs<NJD>& d) {
+  const int lane = threadIdx.x & 63;
+  const int row = n0 + (lane >> 3), c = lane & 7;
+  const int NB = I / 32;
+  const size_t rowc = I / 2, rows = I / 32;
+#pragma unroll
+  for (int j = 0; j < NJD; ++j) {
+    const int b = c + 8 * j;
+    d.cw[j] = (b < NB) ? ld16(C + row * rowc + (size_t)b * 16) : make_uint4(0, 0, 0, 0);
+    d.sb[j] = (b < NB) ? (uint32_t)S[row * rows + b] : 127u;
+  }
+}
+
+// acc += wt * (W a) over this lane's MX blocks of its row (a: fp32 [I] in LDS).
+template <int NJD>
+__device__ __forceinline__ float down_dot(const DownRegs<NJD>& d, const float* a, int I, float wt, float acc) {
+  const int c = threadIdx.x & 7;
+  const int NB = I / 32;
+#pragma unroll
+  for (int j = 0; j < NJD; ++j) {
+    const int b = c + 8 * j;
+    if (b < NB) {
+      const uint32_t w[4] = {d.cw[j].x, d.cw[j].y, d.cw[j].z, d.cw[j].w};
+      const float4* ap = reinterpret_cast<const float4*>(a + b * 36);   // 144-byte blocks
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 a0 = ap[2 * q];
+        const float4 a1 = ap[2 * q + 1];
+        const f32x2_t p0 = fp4x2_to_f32x2<0>(w[q]);
+        const f32x2_t p1 = fp4x2_to_f32x2<1>(w[q]);
+        const f32x2_t p2 = fp4x2_to_f32x2<2>(w[q]);
+        const f32x2_t p3 = fp4x2_to_f32x2<3>(w[q]);
+        s0 = fmaf(p0.x, a0.x, s0);
+        s1 = fmaf(p0.y, a0.y, s1);
+        s0 = fmaf(p1.x, a0.z, s0);
+        s1 = fmaf(p1.y, a0.w, s1);
+        s0 = fmaf(p2.x, a1.x, s0);
+        s1 = fmaf(p2.y, a1.y, s1);
+        s0 = fmaf(p3.x, a1.z, s0);
+        s1 = fmaf(p3.y, a1.w, s1);
+      }
+      acc = fmaf(wt * e8m0_to_f32(d.sb[j]), s0 + s1, acc);
+    }
+  }
+  return acc;
+}
+
+// One wavefront waits until slot s's I activations carry `tag` and copies
+// them to LDS (as fp32).  QA 16-byte chunks (two pairs each) per lane cover
+// the I/2 chunks, all in flight together.
+template <int QA>
+__device__ __forceinline__ void wave_wait_slot(const FusedStepArgs& A, int s, unsigned tag, float* as_slot) {
+  const int lane = threadIdx.x & 63;
+  const int I = A.I;
+  const int nq = I / 2;
+  const uint2* src = a_buf(A, my_copy(kCopiesA)) + (size_t)s * I;
+  // sleep until the slot's last tile has been written, then poll the whole slot
+  if (lane == 0) sleep_on_tag(A, src, I - 1, tag);
+  uint4 p[QA];
+  for (int it = 0;; ++it) {
+    int ok = 1;
+#pragma unroll
+    for (int i = 0; i < QA; ++i) {
+      const int q = lane + 64 * i;
+      p[i] = make_uint4(0, 0, 0, 0);
+      if (q < nq) {
+        p[i] = ld_coh16(src, (uint32_t)q * 16);
+        ok &= (p[i].y == tag) & (p[i].w == tag);
+      }
+    }
+    if (__all(ok)) break;
+    if (wave_should_bail(A, it)) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+#pragma unroll
+  for (int i = 0; i < QA; ++i) {
+    const int q = lane + 64 * i;
+    if (q < nq) {
+      *reinterpret_cast<float2*>(as_slot + apos(0, 2 * q, I)) = make_float2(__uint_as_float(p[i].x), __uint_as_float(p[i].z));
+    }
+  }
+}
+
+// One wavefront waits for all of its routed slots (s = wave + 4 i < k) at once
+// and copies their activations to LDS.
+template <int QA, int MAXR>
+__device__ __forceinline__ void wave_wait_routed(const FusedStepArgs& A, unsigned tag, float* as) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int I = A.I, k = A.k;
+  const int nq = I / 2;
+  const uint2* abuf = a_buf(A, my_copy(kCopiesA));
+  int last = -1;
+#pragma unroll
+  for (int i = 0; i < MAXR; ++i)
+    if (wave + 4 * i < k) last = wave + 4 * i;
+  if (last < 0) return;
+  if (lane == 0) sleep_on_tag(A, abuf + (size_t)last * I, I - 1, tag);
+  uint4 p[MAXR][QA];
+  for (int it = 0;; ++it) {
+    int ok = 1;
+#pragma unroll
+    for (int i = 0; i < MAXR; ++i) {
+      const int s = wave + 4 * i;
+#pragma unroll
+      for (int j = 0; j < QA; ++j) {
+        const int q = lane + 64 * j;
+        p[i][j] = make_uint4(0, 0, 0, 0);
+        if (s < k && q < nq) {
+          p[i][j] = ld_coh16(abuf + (size_t)s * I, (uint32_t)q * 16);
+          ok &= (p[i][j].y == tag) & (p[i][j].w == tag);
+        }
+      }
+    }
+    if (__all(ok)) break;
+    if (wave_should_bail(A, it)) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+#pragma unroll
+  for (int i = 0; i < MAXR; ++i) {
+    const int s = wave + 4 * i;
+#pragma unroll
+    for (int j = 0; j < QA; ++j) {
+      const int q = lane + 64 * j;
+      if (s < k && q < nq) {
+        *reinterpret_cast<float2*>(as + apos(s, 2 * q, I)) =
+            make_float2(__uint_as_float(p[i][j].x), __uint_as_float(p[i][j].z));
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- roles
+
+// R: 8 router rows of layer l (RB-byte elements: 2 = bf16, 4 = fp32); 32 lanes
+// per row, 16-byte granules c, c+32, ...
+template <int RJ, int QPT, int SPL, int RB>
+__device__ __forceinline__ void role_router(const FusedStepArgs& A, int l, int r, unsigned base, uint16_t* xs,
+                                            float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int H = A.H, E = A.E;
+  const int row = r * kRRows + 2 * wave + (lane >> 5);
+  const int c = lane & 31;
+  const int G = H * RB / 16;   // granules per row
+  uint4 wr[RJ];
+  const uint8_t* W = reinterpret_cast<const uint8_t*>(A.router) + ((size_t)l * E + row) * (size_t)H * RB;
+#pragma unroll
+  for (int j = 0; j < RJ; ++j) {
+    const int g = c + 32 * j;
+    wr[j] = g < G ? ld16(W + (size_t)g * 16) : make_uint4(0, 0, 0, 0);
+  }
+  issue_here();
+  // the previous layer's gate/up stage completes before its down stage can:
+  // sleep on it first
+  if (l > 0 && threadIdx.x == 0)
+    sleep_on_tag(A, a_buf(A, my_copy(kCopiesA)), (A.k - 1) * A.I + A.I - 1, base + l - 1);
+  get_u<QPT, SPL, LayPlain>(A, l, base, xs, red);
+  if (l == 0 && r == 0 && A.h_trace)
+    for (int i = threadIdx.x; i < H; i += NT) A.h_trace[i] = A.h_in[i];
+  if (r == 0 && A.u_trace)
+    for (int i = threadIdx.x; i < H; i += NT) A.u_trace[(size_t)l * H + i] = xs[i];
+  const uint32_t* xs32 = reinterpret_cast<const uint32_t*>(xs);
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < RJ; ++j) {
+    const int g = c + 32 * j;
+    if (g < G) {
+      if constexpr (RB == 2) acc += bf16_granule_dot(wr[j], xs32 + g * 4);
+      else acc += f32_granule_dot(wr[j], xs32 + g * 2);
+    }
+  }
+  // rows of 32 lanes: the DPP tree within each 16-lane row, then the pair
+  acc = sum16(acc);
+  const float r0 = readlane_f(acc, 0) + readlane_f(acc, 16);
+  const float r1 = readlane_f(acc, 32) + readlane_f(acc, 48);
+  if (lane < kCopiesLg) {   // lane c publishes copy c
+    const int row0 = r * kRRows + 2 * wave;
+    st_coh16(lg_buf(A, lane), (uint32_t)row0 * 8,
+             make_uint4(__float_as_uint(r0), base + l, __float_as_uint(r1), base + l));
+  }
+}
+
+// S: 16 intermediate values of the shared expert of layer l.
+template <int NJ, int QPT, int SPL>
+__device__ __forceinline__ void role_shared_gateup(const FusedStepArgs& A, int l, int t, unsigned base, uint16_t* xs,
+                                                   float* red) {
+  const int H = A.H, I = A.I;
+  GateUpRegs<NJ> g;
+  gateup_load<NJ>(A.sh13c + (size_t)l * 2 * I * (H / 2), A.sh13s + (size_t)l * 2 * I * (H / 32), H, I, t * kGRows, g);
+  issue_here();
+  if (l > 0 && threadIdx.x == 0) sleep_on_tag(A, a_buf(A, my_copy(kCopiesA)), (A.k - 1) * I + I - 1, base + l - 1);
+  get_u<QPT, SPL, LayMX>(A, l, base, xs, red);
+  gateup_compute<NJ>(g, reinterpret_cast<const uint32_t*>(xs), H, t * kGRows, A.b.a + (size_t)A.k * I,
+                     (size_t)A.nslot * I, base + l);
+}
+
+// G: 16 intermediate values of routed slot s of layer l.
+template <int NJ, int QPT, int SPL, int EPL, int NW>
+__device__ __forceinline__ void role_routed_gateup(const FusedStepArgs& A, int l, int s, int t, unsigned base,
+                                                   uint16_t* xs, float* red, Routing* R) {
+  const int H = A.H, I = A.I;
+  // the layer input is needed by the router too, so it is complete before the
+  // routing can be: sleep on it, normalize it, then wait for the routing
+  if (l > 0 && threadIdx.x == 0) sleep_on_tag(A, hx_buf(A, l, my_copy(kCopiesH)), H / 2 - 1, base + l - 1);
+  __syncthreads();
+  get_u<QPT, SPL, LayMX>(A, l, base, xs, red);
+  block_route<EPL>(A, base + l, R);
+  // clamped: after a failed wait the routing is garbage, but reads stay in bounds
+  const int e = min(max(R->sid[s], 0), A.E - 1);
+  GateUpRegs<NJ> g;
+  const size_t c13 = (size_t)2 * I * (H / 2), s13 = (size_t)2 * I * (H / 32);
+  gateup_load<NJ>(A.w13c + ((size_t)l * A.E + e) * c13, A.w13s + ((size_t)l * A.E + e) * s13, H, I, t * kGRows, g);
+  gateup_compute<NJ>(g, reinterpret_cast<const uint32_t*>(xs), H, t * kGRows, A.b.a + (size_t)s * I,
+                     (size_t)A.nslot * I, base + l);
+}
+
+// D: 8 output rows of layer l over every slot, the weighted combine, the
+// residual add and the tagged store of h_{l+1}.  Wavefront w owns slots w,
+// w+4, w+8 and handles the shared expert's slot (ready early) before its
+// routed slots, always in that fixed order.
+template <int NJD, int EPL, int NW, int QA>
+__device__ __forceinline__ void role_down(const FusedStepArgs& A, int l, int d, unsigned base, float* as,
+                                          Routing* R, float* part) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int H = A.H, I = A.I, E = A.E, k = A.k, nslot = A.nslot;
+  const int n0 = d * kDRows;
+  const unsigned tag = base + l;
+  const size_t c2 = (size_t)H * (I / 2), s2 = (size_t)H * (I / 32);
+  constexpr int MAXS = (WSX_MAX_K + 1 + 3) / 4;   // slots per wavefront: s = wave + 4 i
+  DownRegs<NJD> dr[MAXS];
+  // prefetch the shared expert's rows (slot k)
+#pragma unroll
+  for (int i = 0; i < MAXS; ++i)
+    if (wave + 4 * i == k && nslot > k) down_load<NJD>(A.sh2c + (size_t)l * c2, A.sh2s + (size_t)l * s2, I, n0, dr[i]);
+  issue_here();
+  if (l > 0 && threadIdx.x == 0) sleep_on_tag(A, hx_buf(A, l, my_copy(kCopiesH)), H / 2 - 1, base + l - 1);
+  __syncthreads();
+  // residual rows of this tile (complete: the stream was waited for above)
+  if (threadIdx.x < kDRows) {
+    const int n = n0 + threadIdx.x;
+    float res;
+    if (l == 0) {
+      res = bf16_bits_to_f32(A.h_in[n]);
+    } else {
+      uint2 p = make_uint2(0, 0);
+      for (int it = 0; it < kSpinMax; ++it) {
+        p = ld_coh8(hx_buf(A, l, my_copy(kCopiesH)), (uint32_t)(n >> 1) * 8);
+        if (p.y == base + l - 1 || ((it & 15) == 15 && err_set(A))) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (p.y != base + l - 1) raise_err(A);
+      res = bf16_bits_to_f32((n & 1) ? (p.x >> 16) : (p.x & 0xFFFFu));
+    }
+    part[4 * kDRows + threadIdx.x] = res;
+  }
+  block_route<EPL>(A, tag, R);
+  if (d == 0 && threadIdx.x < k) {
+    if (A.ids_trace) A.ids_trace[(size_t)l * k + threadIdx.x] = R->rid[threadIdx.x];
+    if (A.w_trace) A.w_trace[(size_t)l * k + threadIdx.x] = R->rw[threadIdx.x];
+  }
+#pragma unroll
+  for (int i = 0; i < MAXS; ++i) {
+    const int s = wave + 4 * i;
+    if (s < k) {
+      const int e = min(max(R->sid[s], 0), E - 1);
+      down_load<NJD>(A.w2c + ((size_t)l * E + e) * c2, A.w2s + ((size_t)l * E + e) * s2, I, n0, dr[i]);
+    }
+  }
+  issue_here();
+  float acc = 0.f;
+  // the shared expert first (owned by wavefront k % 4; its activations are
+  // ready early), then the routed slots
+#pragma unroll
+  for (int i = 0; i < MAXS; ++i) {
+    const int s = wave + 4 * i;
+    if (s == k && s < nslot) {
+      wave_wait_slot<QA>(A, s, tag, as + apos(s, 0, I));
+      acc = down_dot<NJD>(dr[i], as + apos(s, 0, I), I, 1.0f, acc);
+    }
+  }
+  wave_wait_routed<QA, (WSX_MAX_K + 3) / 4>(A, tag, as);
+#pragma unroll
+  for (int i = 0; i < MAXS; ++i) {
+    const int s = wave + 4 * i;
+    if (s < k) acc = down_dot<NJD>(dr[i], as + apos(s, 0, I), I, R->sw[s], acc);
+  }
+  acc = sum8(acc);
+  if ((lane & 7) == 0) part[wave * kDRows + (lane >> 3)] = acc;
+  __syncthreads();
+  if (threadIdx.x < kDRows / 2 * kCopiesH) {   // thread (copy c, pair q)
+    const int q = threadIdx.x % (kDRows / 2), cpy = threadIdx.x / (kDRows / 2);
+    uint32_t hb[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int rr = 2 * q + m;
+      const float y = ((part[rr] + part[kDRows + rr]) + part[2 * kDRows + rr]) + part[3 * kDRows + rr];
+      hb[m] = f32_to_bf16_rne(part[4 * kDRows + rr] + y);
+    }
+    const int n = n0 + 2 * q;
+    st_coh8(hx_buf(A, l + 1, cpy), (uint32_t)(n >> 1) * 8, make_uint2(hb[0] | (hb[1] << 16), tag));
+    if (cpy == 0 && A.h_trace) {
+      A.h_trace[(size_t)(l + 1) * H + n] = (uint16_t)hb[0];
+      A.h_trace[(size_t)(l + 1) * H + n + 1] = (uint16_t)hb[1];
+    }
+    if (cpy == 0 && l == A.L - 1) {
+      A.h_out[n] = (uint16_t)hb[0];
+      A.h_out[n + 1] = (uint16_t)hb[1];
+    }
+  }
+  if (threadIdx.x < kCopiesH) {
+    // the tile's sum of squares of h_{l+1} (as rounded to bf16), rows in order
+    float ss = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < kDRows; ++rr) {
+      const float y = ((part[rr] + part[kDRows + rr]) + part[2 * kDRows + rr]) + part[3 * kDRows + rr];
+      const float hv = bf16_bits_to_f32(f32_to_bf16_rne(part[4 * kDRows + rr] + y));
+      ss = fmaf(hv, hv, ss);
+    }
+    st_coh8(ss_buf(A, l + 1, threadIdx.x), (uint32_t)d * 8, make_uint2(__float_as_uint(ss), tag));
+  }
+}
+
+// Head rows: wavefront row groups of 4 rows, 16 lanes per row, HJ granules of
+// 16 codes per lane; the next group's loads are in flight while the current
+// one is reduced.
+template <int HJ>
+__device__ __forceinline__ void head_load(const FusedStepArgs& A, int grp, uint4 (&w)[HJ], float& sc) {
+  const int lane = threadIdx.x & 63;
+  const int row = grp * 4 + (lane >> 4), c = lane & 15;
+  const int G = A.H / 16;
+  const bool ok = row < A.V;
+#pragma unroll
+  for (int j = 0; j < HJ; ++j) {
+    const int g = c + 16 * j;
+    w[j] = (ok && g < G) ? ld16(A.hq + (size_t)row * A.H + (size_t)g * 16) : make_uint4(0, 0, 0, 0);
+  }
+  sc = (ok && c == 0) ? A.hs[row] : 0.f;
+}
+
+template <int HJ, int QPT, int SPL>
+__device__ __forceinline__ void role_head(const FusedStepArgs& A, int hb, unsigned base, uint16_t* xs, float* red,
+                                          float* wv_, int* wi_, int* flag) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int H = A.H, V = A.V, L = A.L;
+  const int NG = (V + 3) / 4;
+  const int stride = A.n_head * 4;
+  const unsigned htag = base + kHeadTag;
+  int grp = hb * 4 + wave;
+  uint4 w[HJ];
+  float sc = 0.f;
+  if (grp < NG) head_load<HJ>(A, grp, w, sc);
+  issue_here();
+  if (threadIdx.x == 0) sleep_on_tag(A, a_buf(A, my_copy(kCopiesA)), (A.k - 1) * A.I + A.I - 1, base + L - 1);
+  wait_u<QPT, SPL, LayHead>(A, L, base + L - 1, xs);
+  if (hb == 0 && A.u_trace)
+    for (int i = threadIdx.x; i < H; i += NT) A.u_trace[(size_t)L * H + i] = xs[LayHead::pos(i)];
+  const uint32_t* xs32 = reinterpret_cast<const uint32_t*>(xs);
+  const int G = H / 16, c = lane & 15;
+  float bv = -INFINITY;
+  int bi = 0x7FFFFFFF;
+  while (grp < NG) {
+    uint4 wn[HJ];
+    float scn = 0.f;
+    const int nxt = grp + stride;
+    if (nxt < NG) head_load<HJ>(A, nxt, wn, scn);
+    issue_here();
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < HJ; ++j) {
+      const int g = c + 16 * j;
+      if (g < G) acc += fp8_granule_dot(w[j], xs32 + g * 12);   // LayHead: 48-byte granules
+    }
+    acc = sum16(acc);
+    const int row = grp * 4 + (lane >> 4);
+    if (c == 0 && row < V) {
+      const float lv = acc * sc;
+      if (A.logits) A.logits[row] = lv;
+      if (better(lv, row, bv, bi)) { bv = lv; bi = row; }
+    }
+#pragma unroll
+    for (int j = 0; j < HJ; ++j) w[j] = wn[j];
+    sc = scn;
+    grp = nxt;
+  }
+  // workgroup argmax
+  wave_argmax(bv, bi);
+  if (lane == 0) { wv_[wave] = bv; wi_[wave] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float v = wv_[0];
+    int i = wi_[0];
+    for (int q = 1; q < 4; ++q)
+      if (better(wv_[q], wi_[q], v, i)) { v = wv_[q]; i = wi_[q]; }
+    st_coh16(A.b.hpart, (uint32_t)hb * 16, make_uint4(__float_as_uint(v), (uint32_t)i, htag, 0));
+  }
+  // first level: the last workgroup of each group of kHeadGroup reduces the group
+  const int gid = hb / kHeadGroup;
+  const int g0 = gid * kHeadGroup;
+  const int gn = min(kHeadGroup, A.n_head - g0);
+  if (!last_block_arrived(A.b.group_counter + gid * 16, gn, flag)) return;
+  if (threadIdx.x < 64) {
+    float v = -INFINITY;
+    int i = 0x7FFFFFFF;
+    if (lane < gn) {
+      const uint4 p = ld_coh16(A.b.hpart, (uint32_t)(g0 + lane) * 16);
+      if (p.z != htag) raise_err(A);
+      v = __uint_as_float(p.x);
+      i = (int)p.y;
+    }
+    wave_argmax(v, i);
+    if (lane == 0) st_coh16(A.b.gpart, (uint32_t)gid * 16, make_uint4(__float_as_uint(v), (uint32_t)i, htag, 0));
+  }
+  // second level: the last group reduces the groups, publishes the argmax and
+  // advances the epoch for the next step
+  if (!last_block_arrived(&ctl(A)->top_counter, A.n_groups, flag)) return;
+  if (threadIdx.x < 64) {
+    float v = -INFINITY;
+    int i = 0x7FFFFFFF;
+    for (int q = lane; q < A.n_groups; q += 64) {
+      const uint4 p = ld_coh16(A.b.gpart, (uint32_t)q * 16);
+      if (p.z != htag) raise_err(A);
+      if (better(__uint_as_float(p.x), (int)p.y, v, i)) { v = __uint_as_float(p.x); i = (int)p.y; }
+    }
+    wave_argmax(v, i);
+    if (lane == 0) {
+      A.argmax[0] = err_set(A) ? -1 : i;
+      const unsigned ep = (unsigned)ld_dev(reinterpret_cast<const int*>(&ctl(A)->epoch));
+      st_dev(reinterpret_cast<int*>(&ctl(A)->epoch), (int)((ep + 1) % kEpochMod));
+    }
+  }
+}
+
+}  // namespace
+
+template <int NJ, int NJD, int RJ, int HJ, int EPL, int NW, int QPT, int QA, int SPL, int RB>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) decode_step_kernel(FusedStepArgs A) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ float red[4];
+  __shared__ Routing R;
+  __shared__ float part[5 * kDRows];
+  __shared__ float wv_[4];
+  __shared__ int wi_[4];
+  __shared__ int flag;
+  // tags: (epoch + 1) in the upper 24 bits, the layer (or 255 for the head) below
+  const unsigned base = ((unsigned)ld_dev(reinterpret_cast<const int*>(&ctl(A)->epoch)) + 1u) << 8;
+  const int bid = A.block0 + (int)blockIdx.x;
+  if (bid >= A.L * A.per_layer) {
+    role_head<HJ, QPT, SPL>(A, bid - A.L * A.per_layer, base, reinterpret_cast<uint16_t*>(smem), red, wv_, wi_, &flag);
+    return;
+  }
+  const int l = bid / A.per_layer;
+  int j = bid - l * A.per_layer;
+  if (j < A.nR) { role_router<RJ, QPT, SPL, RB>(A, l, j, base, reinterpret_cast<uint16_t*>(smem), red); return; }
+  j -= A.nR;
+  if (j < A.nS) { role_shared_gateup<NJ, QPT, SPL>(A, l, j, base, reinterpret_cast<uint16_t*>(smem), red); return; }
+  j -= A.nS;
+  if (j < A.nG) {
+    const int tiles = A.I / kGRows;
+    role_routed_gateup<NJ, QPT, SPL, EPL, NW>(A, l, j / tiles, j % tiles, base, reinterpret_cast<uint16_t*>(smem), red,
+                                         &R);
+    return;
+  }
+  j -= A.nG;
+  role_down<NJD, EPL, NW, QA>(A, l, j, base, reinterpret_cast<float*>(smem), &R, part);
+}
+
+// ---------------------------------------------------------------- host side
+
+namespace {
+
+struct Shape {
+  int NJ, NJD, RJ, HJ, EPL, NW, QPT, QA, SPL;
+};
+
+Shape fused_shape(int H, int I, int E, int router_bytes) {
+  Shape s;
+  s.NJ = (H / 32 + 15) / 16;
+  s.NJD = (I / 32 + 7) / 8;
+  s.RJ = (H * router_bytes / 16 + 31) / 32;
+  s.HJ = (H / 16 + 15) / 16;
+  s.NW = 1;
+  s.EPL = (E + 63) / 64;
+  s.QPT = (H / 4 + NT - 1) / NT;
+  s.QA = (I / 2 + 63) / 64;
+  s.SPL = (H / kDRows / 2 + 63) / 64;
+  return s;
+}
+
+bool is_ling(const Shape& s) {
+  return s.NJ == 5 && s.NJD == 3 && s.RJ == 10 && s.HJ == 10 && s.EPL == 8 && s.NW == 1 && s.QPT == 3 && s.QA == 6 && s.SPL == 3;
+}
+bool is_tiny(const Shape& s) {
+  return s.NJ == 1 && s.NJD == 1 && s.RJ == 2 && s.HJ == 1 && s.EPL == 1 && s.NW == 1 && s.QPT == 1 && s.QA == 1 && s.SPL == 1;
+}
+
+inline size_t al(size_t n) { return (n + 255) & ~(size_t)255; }
+
+struct FusedLayout {
+  size_t ctl, gcnt, hx, ssx, lg, a, hpart, gpart, total;
+  int n_head, n_groups;
+};
+
+int fused_head_blocks(int V) {
+  const int NG = (V + 3) / 4;
+  const int n = (NG + 4 * 8 - 1) / (4 * 8);   // about 8 row groups per wavefront
+  return n < 1 ? 1 : (n > 1024 ? 1024 : n);
+}
+
+FusedLayout fused_layout(int H, int I, int E, int k, int V) {
+  FusedLayout f;
+  const int nslot = k + 1;
+  f.n_head = fused_head_blocks(V);
+  f.n_groups = (f.n_head + kHeadGroup - 1) / kHeadGroup;
+  f.ctl = 0;
+  f.gcnt = al(f.ctl + sizeof(Ctl));
+  f.hx = al(f.gcnt + (size_t)f.n_groups * 64);
+  f.ssx = al(f.hx + (size_t)kCopiesH * 2 * (H / 2) * 8);
+  f.lg = al(f.ssx + (size_t)kCopiesH * 2 * (H / kDRows) * 8);
+  f.a = al(f.lg + (size_t)kCopiesLg * E * 8);
+  f.hpart = al(f.a + (size_t)kCopiesA * nslot * I * 8);
+  f.gpart = al(f.hpart + (size_t)f.n_head * 16);
+  f.total = al(f.gpart + (size_t)f.n_groups * 16);
+  return f;
+}
+
+size_t fused_lds_bytes(int H, int I, int k) {
+  size_t m = (size_t)(k + 1) * (I / 32) * 144;   // expert activations, 144-byte blocks
+  const size_t u[3] = {(size_t)LayPlain::bytes(H), (size_t)LayMX::bytes(H), (size_t)LayHead::bytes(H)};
+  for (size_t v : u) m = v > m ? v : m;
+  return m;
+}
+
+}  // namespace
+
+// Compiled instantiations: the Ling shape with a bf16 router and the tiny
+// shape with an fp32 router; anything else takes the per-phase launches.
+bool fused_step_supported(int T, int router_dtype, bool has_shared, int H, int I, int E, int k) {
+  if (T != 1 || !has_shared) return false;
+  if (E % kRRows || I % kGRows || H % kDRows || k < 1 || k > WSX_MAX_K || k > E) return false;
+  const int rb = router_dtype == WSX_DTYPE_F32 ? 4 : 2;
+  const Shape s = fused_shape(H, I, E, rb);
+  if (!((is_ling(s) && rb == 2) || (is_tiny(s) && rb == 4))) return false;
+  return fused_lds_bytes(H, I, k) <= 64 * 1024;
+}
+
+size_t fused_step_workspace_bytes(int H, int I, int E, int k, int V) { return fused_layout(H, I, E, k, V).total; }
+
+hipError_t launch_fused_step(const wsx_moe_stack* sk, const uint16_t* h_in, const uint8_t* hq, const float* hs, int V,
+                             uint16_t* h_out, float* logits, int32_t* argmax, uint16_t* h_trace, uint16_t* u_trace,
+                             int32_t* ids_trace, float* w_trace, void* ws, hipStream_t st, int segments) {
+  const int L = sk->L, H = sk->H, I = sk->I, E = sk->E, k = sk->k;
+  const FusedLayout f = fused_layout(H, I, E, k, V);
+  char* base = reinterpret_cast<char*>(ws);
+  FusedStepArgs A;
+  A.router = sk->w_router;
+  A.w13c = sk->w13_codes; A.w13s = sk->w13_scales; A.w2c = sk->w2_codes; A.w2s = sk->w2_scales;
+  A.sh13c = sk->sh13_codes; A.sh13s = sk->sh13_scales; A.sh2c = sk->sh2_codes; A.sh2s = sk->sh2_scales;
+  A.hq = hq; A.hs = hs; A.h_in = h_in; A.h_out = h_out; A.logits = logits; A.argmax = argmax;
+  A.h_trace = h_trace; A.u_trace = u_trace; A.ids_trace = ids_trace; A.w_trace = w_trace;
+  A.b.ctl = base + f.ctl;
+  A.b.group_counter = reinterpret_cast<unsigned*>(base + f.gcnt);
+  A.b.hx = reinterpret_cast<uint2*>(base + f.hx);
+  A.b.ssx = reinterpret_cast<uint2*>(base + f.ssx);
+  A.b.lg = reinterpret_cast<uint2*>(base + f.lg);
+  A.b.a = reinterpret_cast<uint2*>(base + f.a);
+  A.b.hpart = reinterpret_cast<uint4*>(base + f.hpart);
+  A.b.gpart = reinterpret_cast<uint4*>(base + f.gpart);
+  A.L = L; A.H = H; A.I = I; A.E = E; A.k = k; A.V = V;
+  A.nslot = k + 1;
+  A.nR = E / kRRows;
+  A.nS = I / kGRows;
+  A.nG = k * (I / kGRows);
+  A.nD = H / kDRows;
+  A.per_layer = A.nR + A.nS + A.nG + A.nD;
+  A.n_head = f.n_head;
+  A.n_groups = f.n_groups;
+  const size_t lds = fused_lds_bytes(H, I, k);
+  const int total = L * A.per_layer + A.n_head;
+  const int rb = sk->router_dtype == WSX_DTYPE_F32 ? 4 : 2;
+  const Shape s = fused_shape(H, I, E, rb);
+  // The workgroups run in one launch (segments = 0), one launch per layer
+  // plus one for the head (1), or one per phase (2); every split respects the
+  // dependency order, so the waits inside simply find their data ready.
+  int cuts[4 * WSX_MAX_LAYERS + 2];
+  int nc = 0;
+  cuts[nc++] = 0;
+  if (segments > 0) {
+    for (int l = 0; l < L; ++l) {
+      const int b = l * A.per_layer;
+      if (segments == 2) {
+        cuts[nc++] = b + A.nR;
+        cuts[nc++] = b + A.nR + A.nS + A.nG;
+      }
+      cuts[nc++] = b + A.per_layer;
+    }
+  }
+  cuts[nc++] = total;
+  for (int c = 0; c + 1 < nc; ++c) {
+    A.block0 = cuts[c];
+    const int grid = cuts[c + 1] - cuts[c];
+    if (grid <= 0) continue;
+    if (is_ling(s) && rb == 2)
+      decode_step_kernel<5, 3, 10, 10, 8, 1, 3, 6, 3, 2><<<grid, NT, lds, st>>>(A);
+    else if (is_tiny(s) && rb == 4)
+      decode_step_kernel<1, 1, 2, 1, 1, 1, 1, 1, 1, 4><<<grid, NT, lds, st>>>(A);
+    else
+      return hipErrorInvalidValue;
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace wsx

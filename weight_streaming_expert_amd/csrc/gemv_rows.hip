@@ -47,7 +47,7 @@ template <int T, int NT>
 __device__ __forceinline__ void stage_input(const uint16_t* __restrict__ x, int K, bool norm, uint16_t* u_out,
                                             uint16_t* xs, float* red) {
   const int tid = threadIdx.x;
-  for (int i = tid; i < T * K; i += NT) xs[i] = x[i];
+  stage_to_lds<NT, (T * 320 + NT - 1) / NT>(x, xs, T * K / 8);
   if (!norm) { __syncthreads(); return; }
   __syncthreads();
 #pragma unroll

@@ -83,7 +83,7 @@ __global__ void __launch_bounds__(256) moe_gateup_kernel(const uint16_t* __restr
     return;
   }
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
-  for (int i = threadIdx.x; i < T * H; i += 256) xs[i] = x[i];
+  stage_to_lds<256, (T * 320 + 255) / 256>(x, xs, T * H / 8);
   __syncthreads();
   const uint32_t* xs32 = reinterpret_cast<const uint32_t*>(xs);
 
@@ -167,10 +167,7 @@ __global__ void __launch_bounds__(256) moe_down_kernel(int H, int I, int E, int 
   const int nslots = n_active + (has_sh ? 1 : 0);
   extern __shared__ __attribute__((aligned(16))) float as[];
   if constexpr (ALDS) {
-    const int n = nslots * T * I;
-    const float4* src = reinterpret_cast<const float4*>(a_in);
-    float4* dst = reinterpret_cast<float4*>(as);
-    for (int i = threadIdx.x; i < n / 4; i += 256) dst[i] = src[i];
+    stage_to_lds<256, 7>(a_in, as, nslots * T * I / 4);
     __syncthreads();
   }
   const float* A = ALDS ? as : a_in;

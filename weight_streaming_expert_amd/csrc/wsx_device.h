@@ -135,6 +135,26 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Sum over the wavefront in one fixed order without LDS traffic: the DPP tree
+// within each row of 16 lanes, then rows 0 + 1 + 2 + 3.  The result is uniform.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v = sum16(v);
+  return ((readlane_f(v, 0) + readlane_f(v, 16)) + readlane_f(v, 32)) + readlane_f(v, 48);
+}
+
+// Maximum over the wavefront (DPP within rows, then the four row maxima).
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_f<kQuadSwap1>(v));
+  v = fmaxf(v, dpp_f<kQuadSwap2>(v));
+  v = fmaxf(v, dpp_f<kRowHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kRowMirror>(v));
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -162,6 +182,69 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g));
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// Copy n16 16-byte chunks from global memory to LDS with NT threads.  Every
+// thread issues all of its loads (at most MAXC) before the first LDS store, so
+// the copy costs one memory latency instead of one per loop trip.  Chunks past
+// MAXC * NT are copied by a plain trailing loop (only reached by callers that
+// pass sizes beyond their fast path).
+template <int NT, int MAXC>
+__device__ __forceinline__ void stage_to_lds(const void* __restrict__ src, void* dst, int n16) {
+  const uint4* s = reinterpret_cast<const uint4*>(src);
+  uint4* d = reinterpret_cast<uint4*>(dst);
+  uint4 v[MAXC];
+#pragma unroll
+  for (int j = 0; j < MAXC; ++j) {
+    const int i = threadIdx.x + j * NT;
+    v[j] = make_uint4(0, 0, 0, 0);
+    if (i < n16) v[j] = s[i];
+  }
+#pragma unroll
+  for (int j = 0; j < MAXC; ++j) {
+    const int i = threadIdx.x + j * NT;
+    if (i < n16) d[i] = v[j];
+  }
+  for (int i = threadIdx.x + MAXC * NT; i < n16; i += NT) d[i] = s[i];
+}
+
+// Wait until every vector memory operation this wave issued has completed, in
+// particular until its device-coherent stores have been acknowledged.  The
+// memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Compiler-only barrier: keeps the loads issued before it (prefetches meant to
+// be in flight during a wait) from being sunk past it to their first use.
+// Emits no instruction and does not wait for the loads.
+__device__ __forceinline__ void issue_here() { asm volatile("" ::: "memory"); }
+
+// Device-coherent (sc1) 8- and 16-byte accesses through buffer instructions.
+// They are performed at the device coherence point, so data written this way
+// by one workgroup is read back current by any other workgroup on any XCD,
+// without cache-wide writeback or invalidation.
+constexpr int kCoherent = 16;   // cache-policy bits: sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
+}
+__device__ __forceinline__ uint4 ld_coh16(const void* base, uint32_t byte_off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(buf_rsrc(base), byte_off, 0, kCoherent));
+}
+__device__ __forceinline__ uint2 ld_coh8(const void* base, uint32_t byte_off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(buf_rsrc(base), byte_off, 0, kCoherent));
+}
+__device__ __forceinline__ void st_coh16(void* base, uint32_t byte_off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v),
+                                         buf_rsrc(base), byte_off, 0, kCoherent);
+}
+__device__ __forceinline__ void st_coh8(void* base, uint32_t byte_off, uint2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, v),
+                                        buf_rsrc(base), byte_off, 0, kCoherent);
+}
+__device__ __forceinline__ void st_coh4(void* base, uint32_t byte_off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, buf_rsrc(base), byte_off, 0, kCoherent);
+}
+__device__ __forceinline__ uint32_t ld_coh4(const void* base, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(base), byte_off, 0, kCoherent);
+}
+
 // Device-coherent accesses for data exchanged between workgroups inside one
 // launch.  Agent-scope relaxed atomics are performed at the device coherence
 // point (they bypass the per-XCD L2 for coherence), so no cache-wide
@@ -174,13 +257,13 @@ __device__ __forceinline__ int ld_dev(const int* p) { return __hip_atomic_load(p
 
 // Last-arriver election.  Every workgroup calls this once, after publishing its
 // partial results with st_dev; exactly one workgroup (the last to arrive) gets
-// true, and may then read every partial with ld_dev.  The workgroup-scope
-// release makes each thread wait until its own device-scope stores are
-// acknowledged; the barrier then covers the whole workgroup before the
-// counter increment.  The winner returns the counter to zero, so it is
-// reusable by the next launch without clearing.
+// true, and may then read every partial with ld_dev.  Each wave first waits
+// until its own device-coherent stores are acknowledged (a workgroup-scope
+// fence alone does not wait for them), the barrier then covers the whole
+// workgroup before the counter increment.  The winner returns the counter to
+// zero, so it is reusable by the next launch without clearing.
 __device__ __forceinline__ bool last_block_arrived(unsigned* counter, unsigned nblocks, int* smem_flag) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  wait_vmem();
   __syncthreads();
   if (threadIdx.x == 0) {
     unsigned old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -10,6 +10,10 @@
 namespace wsx {
 
 constexpr int kHeadMaxGrid = 1024;   // workgroups of the LM-head GEMV (argmax partials)
+constexpr int WSX_MAX_LAYERS = 256;   // stacked layers per decode step (tags hold the layer in 8 bits)
+// How the single-launch decode step is split into launches: 0 = one launch,
+// 1 = one per layer plus the head, 2 = one per phase.
+constexpr int kStepSegments = 0;
 
 // gemv_rows.hip
 bool head_shape_supported(int wt, int K);           // wt: 0 fp8, 1 bf16
@@ -29,6 +33,13 @@ hipError_t launch_gateup(const uint16_t* x, int T, int H, int I, int E, int k, c
 hipError_t launch_down(int T, int H, int I, int E, int k, const uint8_t* w2c, const uint8_t* w2s,
                        const uint8_t* sh2c, const uint8_t* sh2s, const int32_t* el, const float* sw, const float* a,
                        const uint16_t* res, float* y, uint16_t* h, uint16_t* h2, hipStream_t st);
+
+// decode_step.hip: the whole 1-token decode step in one launch
+bool fused_step_supported(int T, int router_dtype, bool has_shared, int H, int I, int E, int k);
+size_t fused_step_workspace_bytes(int H, int I, int E, int k, int V);
+hipError_t launch_fused_step(const wsx_moe_stack* sk, const uint16_t* h_in, const uint8_t* hq, const float* hs, int V,
+                             uint16_t* h_out, float* logits, int32_t* argmax, uint16_t* h_trace, uint16_t* u_trace,
+                             int32_t* ids_trace, float* w_trace, void* ws, hipStream_t st, int segments);
 
 // lm_head_quant.hip
 hipError_t launch_quant_fp8(const uint16_t* w, int V, int K, uint8_t* q, float* s, hipStream_t st);
