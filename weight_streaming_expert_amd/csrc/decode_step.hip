@@ -45,6 +45,9 @@ namespace {
 
 constexpr int NT = 256;            // threads per workgroup
 constexpr int kRRows = 8;          // router rows per R workgroup
+constexpr int kRouteGroups = 2 * NT / 8;   // groups of 8 logits in the routing (E <= 2 NT)
+constexpr int kRouteCand = 8;      // groups whose logits are ranked in full (>= k)
+static_assert(kRouteCand >= WSX_MAX_K && kRouteCand * 8 == kRouteGroups, "routing candidate layout");
 constexpr int kGRows = 16;         // intermediate values per S/G workgroup
 constexpr int kDRows = 8;          // output rows per D workgroup
 constexpr int kHeadGroup = 32;     // head workgroups per first-level argmax group
@@ -360,7 +363,14 @@ __device__ __forceinline__ void rms_norm_inplace(uint16_t* xs, int H, float* red
 
 // ---------------------------------------------------------------- routing
 
-struct Routing {
+struct RankedLogit {
+  float v;
+  int id;
+};
+struct alignas(16) Routing {
+  RankedLogit grp[kRouteGroups];   // best logit of each group of 8
+  RankedLogit cand[kRouteGroups];  // all logits of the kRouteCand best groups
+  float rv[WSX_MAX_K];     // selected logits in rank order
   int rid[WSX_MAX_K];      // selected ids in rank order
   float rw[WSX_MAX_K];     // routing weights in rank order
   int sid[WSX_MAX_K];      // selected ids, ascending (slot order)
@@ -375,98 +385,103 @@ __device__ __forceinline__ void cmpswap(float& va, int& ia, float& vb, int& ib) 
   }
 }
 
-// Top-k routing of one layer: wavefront 0 waits until the E logits carry
-// `tag` (lane L holds logits L*EPL .. L*EPL+EPL-1), sorts its EPL values, then
-// takes k rounds of a DPP wavefront maximum over the lanes' heads (equal
-// maxima go to the lowest lane, whose ids are the lowest, and within a lane
-// the sort keeps ids ascending).  The selected logits, the softmax over them
-// and the ascending slot order are all computed on wavefront-uniform values
-// in registers; the result is left in LDS for the whole workgroup.
-template <int EPL>
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) { return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false); }
+
+// Keep the better of (v, i) and its partner lane's pair under quad_perm CTRL.
+template <int CTRL>
+__device__ __forceinline__ void quad_best(float& v, int& i) {
+  const float ov = dpp_f<CTRL>(v);
+  const int oi = dpp_i<CTRL>(i);
+  if (better(ov, oi, v, i)) { v = ov; i = oi; }
+}
+
+// Number of entries of t[0..15] that rank before (v, i): larger value, then
+// lower id.
+__device__ __forceinline__ int count_better16(const RankedLogit* t, float v, int i) {
+  int n = 0;
+#pragma unroll
+  for (int j = 0; j < 16; j += 2) {
+    const uint4 p = *reinterpret_cast<const uint4*>(t + j);
+    n += better(__uint_as_float(p.x), (int)p.y, v, i);
+    n += better(__uint_as_float(p.z), (int)p.w, v, i);
+  }
+  return n;
+}
+
+// Top-k routing of one layer by the whole workgroup, with no sequential
+// selection rounds ([genai] and [sns], the router: softmax over the k largest
+// of the E expert logits).  Logits rank by value, then by lower id.  Thread t
+// holds logits 2t and 2t+1 (E <= 2 NT; positions past E hold -inf), and each
+// four consecutive threads form a group of 8.  A logit whose group's best
+// logit is beaten by the best logits of k other groups is itself beaten by k
+// logits, so the top k lie in the kRouteCand (>= k) groups whose best logits
+// rank highest.  Both rankings, of the 64 group maxima and then of the 64
+// logits of those groups, count pairwise wins (16 per thread, summed over the
+// group's four threads), so every rank is found at once.  The k selected
+// logits are then normalized by a softmax taken in rank order, and the slot
+// order (ascending ids) is their rank among the selected ids.  The result is
+// left in LDS for the whole workgroup.
 __device__ __forceinline__ void block_route(const FusedStepArgs& A, unsigned tag, Routing* R) {
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    const int E = A.E, k = A.k;
-    const int e0 = lane * EPL;
-    const uint2* lgc = lg_buf(A, my_copy(kCopiesLg));
-    float v[EPL];
-    int id[EPL];
-    for (int it = 0;; ++it) {
-      int ok = 1;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        id[i] = e0 + i < E ? e0 + i : 0x7FFFFFFF;
-        v[i] = -INFINITY;
-      }
-      if constexpr (EPL % 2 == 0) {
-#pragma unroll
-        for (int i = 0; i < EPL; i += 2) {
-          if (e0 + i < E) {
-            const uint4 q = ld_coh16(lgc, (uint32_t)(e0 + i) * 8);
-            v[i] = __uint_as_float(q.x);
-            v[i + 1] = __uint_as_float(q.z);
-            ok &= (q.y == tag) & (q.w == tag);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-          if (e0 + i < E) {
-            const uint2 q = ld_coh8(lgc, (uint32_t)(e0 + i) * 8);
-            v[i] = __uint_as_float(q.x);
-            ok &= (q.y == tag);
-          }
-        }
-      }
-      if (__all(ok)) break;
-      if (wave_should_bail(A, it)) break;
-      __builtin_amdgcn_s_sleep(1);
+  const int t = threadIdx.x, q = t & 3, E = A.E, k = A.k;
+  const int e0 = 2 * t;
+  const uint2* lgc = lg_buf(A, my_copy(kCopiesLg));
+  float v0 = -INFINITY, v1 = -INFINITY;
+  for (int it = 0;; ++it) {
+    int ok = 1;
+    if (e0 < E) {   // E is even: both logits of the pair exist
+      const uint4 w = ld_coh16(lgc, (uint32_t)e0 * 8);
+      v0 = __uint_as_float(w.x);
+      v1 = __uint_as_float(w.z);
+      ok = (w.y == tag) & (w.w == tag);
     }
-    // lane-local sort (fixed network over compile-time indices)
-#pragma unroll
-    for (int i = 0; i < EPL; ++i)
-#pragma unroll
-      for (int j = 0; j < EPL - 1 - i; ++j) cmpswap(v[j], id[j], v[j + 1], id[j + 1]);
-    float top[WSX_MAX_K];
-    int topi[WSX_MAX_K];
+    if (__all(ok)) break;
+    if (wave_should_bail(A, it)) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  // best logit of the group (every thread of the four ends with it)
+  float bv = v0;
+  int bi = e0;
+  if (better(v1, e0 + 1, bv, bi)) { bv = v1; bi = e0 + 1; }
+  quad_best<kQuadSwap1>(bv, bi);
+  quad_best<kQuadSwap2>(bv, bi);
+  if (q == 0) R->grp[t >> 2] = RankedLogit{bv, bi};
+  __syncthreads();
+  int rank = count_better16(R->grp + 16 * q, bv, bi);
+  rank += dpp_i<kQuadSwap1>(rank);
+  rank += dpp_i<kQuadSwap2>(rank);
+  if (rank < kRouteCand) {
+    *reinterpret_cast<uint4*>(R->cand + rank * 8 + 2 * q) =
+        make_uint4(__float_as_uint(v0), (unsigned)e0, __float_as_uint(v1), (unsigned)(e0 + 1));
+  }
+  __syncthreads();
+  const RankedLogit me = R->cand[t >> 2];
+  rank = count_better16(R->cand + 16 * q, me.v, me.id);
+  rank += dpp_i<kQuadSwap1>(rank);
+  rank += dpp_i<kQuadSwap2>(rank);
+  if (q == 0 && rank < k) {
+    R->rv[rank] = me.v;
+    R->rid[rank] = me.id;
+  }
+  __syncthreads();
+  if (t < k) {
+    const int myid = R->rid[t];
+    const float top = R->rv[0];
+    float zs = 0.f, mine = 0.f;
+    int slot = 0;
 #pragma unroll
     for (int j = 0; j < WSX_MAX_K; ++j) {
-      top[j] = -INFINITY;
-      topi[j] = 0x7FFFFFFF;
       if (j < k) {
-        const float m = wave_max_dpp(v[0]);
-        const unsigned long long owners = __ballot(v[0] == m);
-        const int owner = __ffsll((long long)owners) - 1;
-        top[j] = m;
-        topi[j] = __builtin_amdgcn_readlane(id[0], owner);
-        if (lane == owner) {
-#pragma unroll
-          for (int i = 0; i < EPL - 1; ++i) { v[i] = v[i + 1]; id[i] = id[i + 1]; }
-          v[EPL - 1] = -INFINITY;
-          id[EPL - 1] = 0x7FFFFFFF;
-        }
+        const float z = __expf(R->rv[j] - top);
+        zs += z;
+        if (j == t) mine = z;
+        slot += R->rid[j] < myid;
       }
     }
-    // softmax over the selected logits, in rank order
-    float z[WSX_MAX_K], zs = 0.f;
-#pragma unroll
-    for (int j = 0; j < WSX_MAX_K; ++j) {
-      z[j] = 0.f;
-      if (j < k) { z[j] = __expf(top[j] - top[0]); zs += z[j]; }
-    }
-    if (lane < k) {
-      int myid = 0, slot = 0;
-      float myw = 0.f;
-#pragma unroll
-      for (int j = 0; j < WSX_MAX_K; ++j)
-        if (j == lane) { myid = topi[j]; myw = z[j] / zs; }
-#pragma unroll
-      for (int j = 0; j < WSX_MAX_K; ++j) slot += (j < k) & (topi[j] < myid);
-      R->rid[lane] = myid;
-      R->rw[lane] = myw;
-      R->sid[slot] = myid;
-      R->sw[slot] = myw;
-    }
+    const float w = mine / zs;
+    R->rw[t] = w;
+    R->sid[slot] = myid;
+    R->sw[slot] = w;
   }
   __syncthreads();
 }
@@ -745,7 +760,7 @@ __device__ __forceinline__ void role_shared_gateup(const FusedStepArgs& A, int l
 }
 
 // G: 16 intermediate values of routed slot s of layer l.
-template <int NJ, int QPT, int SPL, int EPL, int NW>
+template <int NJ, int QPT, int SPL>
 __device__ __forceinline__ void role_routed_gateup(const FusedStepArgs& A, int l, int s, int t, unsigned base,
                                                    uint16_t* xs, float* red, Routing* R) {
   const int H = A.H, I = A.I;
@@ -754,7 +769,7 @@ __device__ __forceinline__ void role_routed_gateup(const FusedStepArgs& A, int l
   if (l > 0 && threadIdx.x == 0) sleep_on_tag(A, hx_buf(A, l, my_copy(kCopiesH)), H / 2 - 1, base + l - 1);
   __syncthreads();
   get_u<QPT, SPL, LayMX>(A, l, base, xs, red);
-  block_route<EPL>(A, base + l, R);
+  block_route(A, base + l, R);
   // clamped: after a failed wait the routing is garbage, but reads stay in bounds
   const int e = min(max(R->sid[s], 0), A.E - 1);
   GateUpRegs<NJ> g;
@@ -768,7 +783,7 @@ __device__ __forceinline__ void role_routed_gateup(const FusedStepArgs& A, int l
 // residual add and the tagged store of h_{l+1}.  Wavefront w owns slots w,
 // w+4, w+8 and handles the shared expert's slot (ready early) before its
 // routed slots, always in that fixed order.
-template <int NJD, int EPL, int NW, int QA>
+template <int NJD, int QA>
 __device__ __forceinline__ void role_down(const FusedStepArgs& A, int l, int d, unsigned base, float* as,
                                           Routing* R, float* part) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -803,7 +818,7 @@ __device__ __forceinline__ void role_down(const FusedStepArgs& A, int l, int d, 
     }
     part[4 * kDRows + threadIdx.x] = res;
   }
-  block_route<EPL>(A, tag, R);
+  block_route(A, tag, R);
   if (d == 0 && threadIdx.x < k) {
     if (A.ids_trace) A.ids_trace[(size_t)l * k + threadIdx.x] = R->rid[threadIdx.x];
     if (A.w_trace) A.w_trace[(size_t)l * k + threadIdx.x] = R->rw[threadIdx.x];
@@ -982,7 +997,7 @@ __device__ __forceinline__ void role_head(const FusedStepArgs& A, int hb, unsign
 
 }  // namespace
 
-template <int NJ, int NJD, int RJ, int HJ, int EPL, int NW, int QPT, int QA, int SPL, int RB>
+template <int NJ, int NJD, int RJ, int HJ, int QPT, int QA, int SPL, int RB>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) decode_step_kernel(FusedStepArgs A) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ float red[4];
@@ -1006,12 +1021,12 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) de
   j -= A.nS;
   if (j < A.nG) {
     const int tiles = A.I / kGRows;
-    role_routed_gateup<NJ, QPT, SPL, EPL, NW>(A, l, j / tiles, j % tiles, base, reinterpret_cast<uint16_t*>(smem), red,
+    role_routed_gateup<NJ, QPT, SPL>(A, l, j / tiles, j % tiles, base, reinterpret_cast<uint16_t*>(smem), red,
                                          &R);
     return;
   }
   j -= A.nG;
-  role_down<NJD, EPL, NW, QA>(A, l, j, base, reinterpret_cast<float*>(smem), &R, part);
+  role_down<NJD, QA>(A, l, j, base, reinterpret_cast<float*>(smem), &R, part);
 }
 
 // ---------------------------------------------------------------- host side
@@ -1019,17 +1034,15 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) de
 namespace {
 
 struct Shape {
-  int NJ, NJD, RJ, HJ, EPL, NW, QPT, QA, SPL;
+  int NJ, NJD, RJ, HJ, QPT, QA, SPL;
 };
 
-Shape fused_shape(int H, int I, int E, int router_bytes) {
+Shape fused_shape(int H, int I, int router_bytes) {
   Shape s;
   s.NJ = (H / 32 + 15) / 16;
   s.NJD = (I / 32 + 7) / 8;
   s.RJ = (H * router_bytes / 16 + 31) / 32;
   s.HJ = (H / 16 + 15) / 16;
-  s.NW = 1;
-  s.EPL = (E + 63) / 64;
   s.QPT = (H / 4 + NT - 1) / NT;
   s.QA = (I / 2 + 63) / 64;
   s.SPL = (H / kDRows / 2 + 63) / 64;
@@ -1037,10 +1050,10 @@ Shape fused_shape(int H, int I, int E, int router_bytes) {
 }
 
 bool is_ling(const Shape& s) {
-  return s.NJ == 5 && s.NJD == 3 && s.RJ == 10 && s.HJ == 10 && s.EPL == 8 && s.NW == 1 && s.QPT == 3 && s.QA == 6 && s.SPL == 3;
+  return s.NJ == 5 && s.NJD == 3 && s.RJ == 10 && s.HJ == 10 && s.QPT == 3 && s.QA == 6 && s.SPL == 3;
 }
 bool is_tiny(const Shape& s) {
-  return s.NJ == 1 && s.NJD == 1 && s.RJ == 2 && s.HJ == 1 && s.EPL == 1 && s.NW == 1 && s.QPT == 1 && s.QA == 1 && s.SPL == 1;
+  return s.NJ == 1 && s.NJD == 1 && s.RJ == 2 && s.HJ == 1 && s.QPT == 1 && s.QA == 1 && s.SPL == 1;
 }
 
 inline size_t al(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -1086,9 +1099,9 @@ size_t fused_lds_bytes(int H, int I, int k) {
 // shape with an fp32 router; anything else takes the per-phase launches.
 bool fused_step_supported(int T, int router_dtype, bool has_shared, int H, int I, int E, int k) {
   if (T != 1 || !has_shared) return false;
-  if (E % kRRows || I % kGRows || H % kDRows || k < 1 || k > WSX_MAX_K || k > E) return false;
+  if (E % kRRows || E > 2 * NT || I % kGRows || H % kDRows || k < 1 || k > WSX_MAX_K || k > E) return false;
   const int rb = router_dtype == WSX_DTYPE_F32 ? 4 : 2;
-  const Shape s = fused_shape(H, I, E, rb);
+  const Shape s = fused_shape(H, I, rb);
   if (!((is_ling(s) && rb == 2) || (is_tiny(s) && rb == 4))) return false;
   return fused_lds_bytes(H, I, k) <= 64 * 1024;
 }
@@ -1127,7 +1140,7 @@ hipError_t launch_fused_step(const wsx_moe_stack* sk, const uint16_t* h_in, cons
   const size_t lds = fused_lds_bytes(H, I, k);
   const int total = L * A.per_layer + A.n_head;
   const int rb = sk->router_dtype == WSX_DTYPE_F32 ? 4 : 2;
-  const Shape s = fused_shape(H, I, E, rb);
+  const Shape s = fused_shape(H, I, rb);
   // The workgroups run in one launch (segments = 0), one launch per layer
   // plus one for the head (1), or one per phase (2); every split respects the
   // dependency order, so the waits inside simply find their data ready.
@@ -1150,9 +1163,9 @@ hipError_t launch_fused_step(const wsx_moe_stack* sk, const uint16_t* h_in, cons
     const int grid = cuts[c + 1] - cuts[c];
     if (grid <= 0) continue;
     if (is_ling(s) && rb == 2)
-      decode_step_kernel<5, 3, 10, 10, 8, 1, 3, 6, 3, 2><<<grid, NT, lds, st>>>(A);
+      decode_step_kernel<5, 3, 10, 10, 3, 6, 3, 2><<<grid, NT, lds, st>>>(A);
     else if (is_tiny(s) && rb == 4)
-      decode_step_kernel<1, 1, 2, 1, 1, 1, 1, 1, 1, 4><<<grid, NT, lds, st>>>(A);
+      decode_step_kernel<1, 1, 2, 1, 1, 1, 1, 4><<<grid, NT, lds, st>>>(A);
     else
       return hipErrorInvalidValue;
     const hipError_t e = hipGetLastError();
