@@ -11,7 +11,8 @@ HBM before timing; each step is one replay of a captured HIP graph on one
 stream, preceded by a 5 KB device copy of that step's token.
 
 Prints one JSON line (rank 0) with the µs per step, the achieved HBM rate of
-the step's algorithmic bytes, the roofline object of the LM-head kernel, a
+the step's algorithmic bytes, the roofline object of the dominant kernel (the
+single-launch decode step), the standalone FP8 head kernel's rate, a
 per-component breakdown (one MoE layer with a cold cache, the FP8 and BF16
 heads, the 4-token verify pass, the load-time quantizer) and the CPU-oracle
 baseline timed on a bounded sample of the same workload.
@@ -44,6 +45,10 @@ def parse():
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--head-reps", type=int, default=200)
+    ap.add_argument("--kernel-reps", type=int, default=200)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the run, copy a buffer of this many MiB device-to-device 3 times (a plain copy "
+                         "kernel of known size, used to scale hardware byte counters)")
     return ap.parse_args()
 
 
@@ -137,7 +142,30 @@ def main():
     gbps = step_bytes / (us_step * 1e-6) / 1e9
     log(f"decode step: {us_step:.1f} us, {gbps:.0f} GB/s ({100 * gbps / PEAK_GBPS:.1f}% of 8 TB/s)")
 
-    # ------------------------------------------------------------------ dominant kernel: FP8 LM head
+    # ------------------------------------------------------------------ dominant kernel: the one-launch step
+    # Ten back-to-back steps per graph, no token copies between them: the
+    # average launch duration of the step kernel itself.
+    gk = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gk):
+        for _ in range(10):
+            ops.moe_decode_step(h_in, stack, head, ws=ws, out=out)
+    gk.replay()
+    torch.cuda.synchronize()
+    reps = max(1, args.kernel_reps // 10)
+    e0.record()
+    for _ in range(reps):
+        gk.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    k_us = e0.elapsed_time(e1) * 1e3 / (10 * reps)
+    k_gbps = step_bytes / (k_us * 1e-6) / 1e9
+    roofline = {"kernel": "decode_step_kernel (one launch: 32 MoE layers + FP8 head with argmax)", "bound": "hbm",
+                "achieved": round(k_gbps, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                "frac": round(k_gbps / PEAK_GBPS, 4), "traffic": step_traffic_bytes(),
+                "bytes_per_launch": step_bytes, "us_per_launch": round(k_us, 2)}
+    log(f"step kernel: {k_us:.1f} us per launch, {k_gbps:.0f} GB/s")
+
+    # ------------------------------------------------------------------ the FP8 LM head kernel on its own
     u = torch.from_numpy(inputs.activations(wl, 0).view(np.int16)).view(torch.bfloat16).to(dev)
     hws = ops.workspace(ops.lm_head_workspace_bytes(1, V, H), dev)
     hlog = torch.empty((1, V), dtype=torch.float32, device=dev)
@@ -164,10 +192,10 @@ def main():
     head_us = e0.elapsed_time(e1) * 1e3 / (10 * reps)
     head_bytes = configs.head_bytes(V, H, 1, True)
     head_gbps = head_bytes / (head_us * 1e-6) / 1e9
-    roofline = {"kernel": "lm_head_kernel<fp8,T=1> (FP8 LM-head GEMV + argmax)", "bound": "hbm",
-                "achieved": round(head_gbps, 1), "peak": PEAK_GBPS, "unit": "GB/s",
-                "frac": round(head_gbps / PEAK_GBPS, 4), "traffic": None,
-                "bytes_per_launch": head_bytes, "us_per_launch": round(head_us, 2)}
+    head_kernel = {"kernel": "lm_head_kernel<fp8,T=1> (FP8 LM-head GEMV + argmax, standalone)", "bound": "hbm",
+                   "achieved": round(head_gbps, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                   "frac": round(head_gbps / PEAK_GBPS, 4), "bytes_per_launch": head_bytes,
+                   "us_per_launch": round(head_us, 2)}
     log(f"fp8 head: {head_us:.1f} us, {head_gbps:.0f} GB/s")
 
     result = {
@@ -180,6 +208,7 @@ def main():
                    "step_bytes": step_bytes},
         "achieved_GBps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_GBPS, 4),
         "roofline": roofline,
+        "head_kernel": head_kernel,
     }
 
     if not args.no_breakdown:
@@ -188,6 +217,47 @@ def main():
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(torch, ops, configs, inputs, dev, stack, head, host_layer0, wl, step_bytes)
     print(json.dumps(result), flush=True)
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: 3 x {args.calib_copy_mib} MiB device-to-device")
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_kernel_hbm_counters.md")
+STEP_SOURCES = ("weight_streaming_expert_amd/csrc/decode_step.hip", "weight_streaming_expert_amd/csrc/wsx_device.h")
+
+
+def step_source_digest():
+    """sha256 over the step kernel's sources, to tell whether recorded counters still apply."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in STEP_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def step_traffic_bytes():
+    """HBM bytes per launch of the step kernel, from the recorded FETCH_SIZE and
+    WRITE_SIZE counter runs (scaled by a plain copy of known size); None when no
+    record exists or the kernel's sources changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and line.startswith("- `"):
+            key, val = line[3:].split("`", 1)
+            rec[key] = val.split(":", 1)[1].strip().strip("`")
+    if rec.get("sources_sha256") != step_source_digest():
+        return None
+    try:
+        return int(rec["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def _timed_graph(torch, fn, flush=None, reps=100):
