@@ -17,14 +17,18 @@ inline hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
 inline wsx_status hip_status(hipError_t e) { return e == hipSuccess ? WSX_OK : WSX_ERR_HIP; }
 
 struct MoeWs {
-  size_t counter, logits, a, total;
+  size_t counter, logits, a, part, dcnt, total;
 };
-MoeWs moe_ws(int T, int I, int E, int k) {
+// counter (router), router logits, expert activations, then the grouped down
+// kernel's partial sums and its per-row-tile counters (64-byte stride)
+MoeWs moe_ws(int T, int H, int I, int E, int k) {
   MoeWs w;
   w.counter = 0;
   w.logits = 256;
   w.a = align256(w.logits + (size_t)T * E * 4);
-  w.total = align256(w.a + (size_t)(T * k + 1) * T * I * 4);
+  w.part = align256(w.a + (size_t)(T * k + 1) * T * I * 4);
+  w.dcnt = align256(w.part + (size_t)down_groups(T * k + 1) * T * H * 4);
+  w.total = align256(w.dcnt + (size_t)(H / 32 + 1) * 64);
   return w;
 }
 size_t head_ws_bytes() { return 256 + (size_t)2 * kHeadMaxGrid * WSX_MAX_T * 4; }
@@ -35,7 +39,7 @@ struct StepWs {
 };
 StepWs step_ws(int T, int H, int I, int E, int k) {
   StepWs s;
-  s.moe = moe_ws(T, I, E, k);
+  s.moe = moe_ws(T, H, I, E, k);
   s.moe_base = 0;
   s.head = align256(s.moe.total);
   s.u = align256(s.head + head_ws_bytes());
@@ -95,7 +99,7 @@ extern "C" {
 size_t wsx_moe_workspace_bytes(int T, int H, int I, int E, int k) {
   (void)H;
   if (T < 1 || T > WSX_MAX_T || k < 1 || k > WSX_MAX_K || E < 1 || E > WSX_MAX_E || I < 0) return 0;
-  return moe_ws(T, I, E, k).total;
+  return moe_ws(T, H, I, E, k).total;
 }
 
 size_t wsx_lm_head_workspace_bytes(int T, int V, int K) {
@@ -115,8 +119,8 @@ wsx_status moe_route_topk(const uint16_t* x, const void* w_router, int router_dt
   wsx_status st = check_router(x, w_router, router_dtype, T, H, E, k);
   if (st != WSX_OK) return st;
   if (!topk_ids || !topk_w || !expert_list || !slot_w) return WSX_ERR_NULL;
-  if ((st = check_ws(ws, ws_bytes, moe_ws(T, 32, E, k).a)) != WSX_OK) return st;
-  const MoeWs L = moe_ws(T, 32, E, k);
+  if ((st = check_ws(ws, ws_bytes, moe_ws(T, H, 32, E, k).a)) != WSX_OK) return st;
+  const MoeWs L = moe_ws(T, H, 32, E, k);
   float* logits = logits_out ? logits_out : reinterpret_cast<float*>((char*)ws + L.logits);
   return hip_status(launch_router(router_dtype, w_router, E, H, k, x, T, 0, nullptr, logits, topk_ids, topk_w,
                                   expert_list, slot_w, reinterpret_cast<unsigned*>((char*)ws + L.counter), S(stream)));
@@ -133,14 +137,16 @@ wsx_status moe_expert_gemv_mxfp4(const uint16_t* x, const uint8_t* w13_codes, co
                                 sh2_scales, T, H, I, E, k);
   if (st != WSX_OK) return st;
   if (out_h && !residual) return WSX_ERR_NULL;
-  const MoeWs L = moe_ws(T, I, E, k);
+  const MoeWs L = moe_ws(T, H, I, E, k);
   if ((st = check_ws(ws, ws_bytes, L.total)) != WSX_OK) return st;
   float* a = reinterpret_cast<float*>((char*)ws + L.a);
+  float* part = reinterpret_cast<float*>((char*)ws + L.part);
+  unsigned* dcnt = reinterpret_cast<unsigned*>((char*)ws + L.dcnt);
   hipError_t e = launch_gateup(x, T, H, I, E, k, w13_codes, w13_scales, sh13_codes, sh13_scales, expert_list, a,
                                S(stream));
   if (e != hipSuccess) return WSX_ERR_HIP;
   return hip_status(launch_down(T, H, I, E, k, w2_codes, w2_scales, sh2_codes, sh2_scales, expert_list, slot_w, a,
-                                residual, out_y, out_h, nullptr, S(stream)));
+                                residual, out_y, out_h, nullptr, part, dcnt, S(stream)));
 }
 
 wsx_status lm_head_quantize_fp8(const uint16_t* w, int V, int K, uint8_t* q, float* row_scale, void* stream) {
@@ -202,6 +208,8 @@ wsx_status moe_decode_step(const uint16_t* h_in, int T, const wsx_moe_stack* sk,
   unsigned* counter = reinterpret_cast<unsigned*>(base + W.moe.counter);
   float* rlogits = reinterpret_cast<float*>(base + W.moe.logits);
   float* a = reinterpret_cast<float*>(base + W.moe.a);
+  float* part = reinterpret_cast<float*>(base + W.moe.part);
+  unsigned* dcnt = reinterpret_cast<unsigned*>(base + W.moe.dcnt);
   int32_t* el = reinterpret_cast<int32_t*>(base + W.el);
   float* sw = reinterpret_cast<float*>(base + W.sw);
   uint16_t* ping[2] = {reinterpret_cast<uint16_t*>(base + W.h0), reinterpret_cast<uint16_t*>(base + W.h1)};
@@ -235,7 +243,7 @@ wsx_status moe_decode_step(const uint16_t* h_in, int T, const wsx_moe_stack* sk,
     if (e != hipSuccess) return WSX_ERR_HIP;
     e = launch_down(T, H, I, E, k, sk->w2_codes + (size_t)l * c2, sk->w2_scales + (size_t)l * s2,
                     sh ? sk->sh2_codes + (size_t)l * sc2 : nullptr, sh ? sk->sh2_scales + (size_t)l * ss2 : nullptr,
-                    el, sw, a, h_cur, nullptr, h_next, h_next2, s);
+                    el, sw, a, h_cur, nullptr, h_next, h_next2, part, dcnt, s);
     if (e != hipSuccess) return WSX_ERR_HIP;
     h_cur = h_next;
   }

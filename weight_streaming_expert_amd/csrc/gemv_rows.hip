@@ -238,91 +238,176 @@ __global__ void __launch_bounds__(256) lm_head_kernel(const uint8_t* __restrict_
 
 // ---------------------------------------------------------------- router + top-k
 
-constexpr int kRouterWaves = 1;   // one wavefront per workgroup spreads the 2.6 MB router over more CUs
+// Top-k of one token's E logits (E <= 4 * 256) by the whole 256-thread
+// workgroup, with no sequential selection rounds.  Logits rank by value, then
+// by lower id.  Thread t holds logits P t .. P t + P - 1 (positions past E
+// hold -inf) and four consecutive threads form a group of 4P.  A logit whose
+// group's best logit is beaten by the best logits of k other groups is itself
+// beaten by k logits, so the top k lie in the 8 (>= k) groups whose best
+// logits rank highest.  The 64 group maxima are ranked by counting pairwise
+// wins (16 comparisons per thread, summed over the group's four threads);
+// then the 32P logits of the 8 best groups are ranked the same way.  Leaves
+// the k (logit, id) pairs in rank order in rv / rid.
+constexpr int kTopkGroups = 64;
+struct alignas(16) TopkScratch {
+  float2 grp[kTopkGroups];   // (best logit, id bits) per group
+  float2 cand[8 * 4 * 4];    // every logit of the 8 best groups (P <= 4)
+  float rv[WSX_MAX_K];
+  int rid[WSX_MAX_K];
+};
 
-template <int WT, int T, int GPL>
-__global__ void __launch_bounds__(64 * kRouterWaves) router_topk_kernel(
+__device__ __forceinline__ bool rank_before(float2 a, float v, int i) {
+  return better(a.x, __float_as_int(a.y), v, i);
+}
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_int(int v) { return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false); }
+
+template <int P>
+__device__ __forceinline__ void block_topk(const float* __restrict__ lrow, int E, int k, TopkScratch* R) {
+  constexpr int NC = 8 * 4 * P;   // candidates
+  constexpr int TPC = 256 / NC;   // threads per candidate (4 or 2)
+  constexpr int CPT = NC / TPC;   // comparisons per thread
+  const int t = threadIdx.x, q = t & 3;
+  const int e0 = P * t;
+  float v[P];
+#pragma unroll
+  for (int i = 0; i < P; ++i) v[i] = (e0 + i < E) ? ld_dev(lrow + e0 + i) : -INFINITY;
+  float bv = v[0];
+  int bi = e0;
+#pragma unroll
+  for (int i = 1; i < P; ++i)
+    if (better(v[i], e0 + i, bv, bi)) { bv = v[i]; bi = e0 + i; }
+  {
+    const float ov = dpp_f<kQuadSwap1>(bv);
+    const int oi = dpp_int<kQuadSwap1>(bi);
+    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+  {
+    const float ov = dpp_f<kQuadSwap2>(bv);
+    const int oi = dpp_int<kQuadSwap2>(bi);
+    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+  if (q == 0) R->grp[t >> 2] = make_float2(bv, __int_as_float(bi));
+  __syncthreads();
+  int rank = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) rank += rank_before(R->grp[16 * q + j], bv, bi);
+  rank += dpp_int<kQuadSwap1>(rank);
+  rank += dpp_int<kQuadSwap2>(rank);
+  if (rank < 8) {
+#pragma unroll
+    for (int i = 0; i < P; ++i) R->cand[rank * 4 * P + P * q + i] = make_float2(v[i], __int_as_float(e0 + i));
+  }
+  __syncthreads();
+  const int ci = t / TPC, part = t % TPC;
+  const float2 me = R->cand[ci];
+  const int mid = __float_as_int(me.y);
+  int r2 = 0;
+#pragma unroll 16
+  for (int j = 0; j < CPT; ++j) r2 += rank_before(R->cand[part * CPT + j], me.x, mid);
+  r2 += dpp_int<kQuadSwap1>(r2);
+  if constexpr (TPC == 4) r2 += dpp_int<kQuadSwap2>(r2);
+  if (part == 0 && r2 < k) {
+    R->rv[r2] = me.x;
+    R->rid[r2] = mid;
+  }
+  __syncthreads();
+}
+
+// Router GEMV with one row per wavefront (64 lanes; lane l takes the 16-byte
+// granules l, l + 64, ...; RGPL per lane) for T tokens staged in LDS (and
+// normalized there when `norm` is set).  Every row uses the same lanes and the
+// same fixed reduction order, so equal rows give bit-identical logits.  The
+// row's weights are requested before the activations are staged, so the two
+// overlap.  The last workgroup to finish then takes, per token, the top-k and
+// the softmax over the selected logits in rank order, and finally builds the
+// compact ascending expert list and the slot weight table.
+template <int WT, int T, int RGPL, int P>
+__global__ void __launch_bounds__(256) router_topk_kernel(
     const uint8_t* __restrict__ W, int E, int K, int k, const uint16_t* __restrict__ x, int norm, uint16_t* u_out,
     float* logits, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, int32_t* __restrict__ expert_list,
     float* __restrict__ slot_w, unsigned* counter) {
-  constexpr int NT = 64 * kRouterWaves, DW = WTraits<WT>::EPG / 2;
+  constexpr int DW = WTraits<WT>::EPG / 2;
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
-  __shared__ float red[T * kRouterWaves * 4];
+  __shared__ float red[T * 4];
   __shared__ int flag;
-  stage_input<T, NT>(x, K, norm != 0, u_out, xs, red);
-  const uint32_t* xs32 = reinterpret_cast<const uint32_t*>(xs);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int G = K / WTraits<WT>::EPG;
   const size_t row_bytes = (size_t)K * WTraits<WT>::ESZ;
-  uint32_t xr[T == 1 ? GPL : 1][DW];
-  if constexpr (T == 1) load_x_regs<WT, GPL>(xs32, G, xr);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int NG = (E + 3) / 4;
-  for (int g0 = blockIdx.x * kRouterWaves + wave; g0 < NG; g0 += gridDim.x * kRouterWaves) {
-    int rg[1] = {g0};
-    float acc[1][T];
-    rows_dot<WT, T, GPL, 1>(W, row_bytes, E, G, rg, xr, xs32, K, acc);
-    const int row = g0 * 4 + (lane >> 4);
-    if ((lane & 15) == 0 && row < E)
+  int row = blockIdx.x * 4 + wave;
+  uint4 wv[RGPL];
 #pragma unroll
-      for (int t = 0; t < T; ++t) st_dev(logits + (size_t)t * E + row, acc[0][t]);
+  for (int j = 0; j < RGPL; ++j) {
+    const int g = lane + 64 * j;
+    wv[j] = (row < E && g < G) ? ld16(W + (size_t)row * row_bytes + (size_t)g * 16) : make_uint4(0, 0, 0, 0);
+  }
+  stage_input<T, 256>(x, K, norm != 0, u_out, xs, red);
+  const uint32_t* xs32 = reinterpret_cast<const uint32_t*>(xs);
+  while (row < E) {
+    float acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[t] = 0.f;
+#pragma unroll
+    for (int j = 0; j < RGPL; ++j) {
+      const int g = lane + 64 * j;
+      if (g < G) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          uint32_t xp[DW];
+          const uint32_t* src = xs32 + (size_t)t * (K / 2) + (size_t)g * DW;
+#pragma unroll
+          for (int d = 0; d < DW; ++d) xp[d] = src[d];
+          acc[t] += granule_dot<WT>(wv[j], xp);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const float s = wave_sum_dpp(acc[t]);
+      if (lane == 0) st_dev(logits + (size_t)t * E + row, s);
+    }
+    row += gridDim.x * 4;
+    if (row < E) {
+#pragma unroll
+      for (int j = 0; j < RGPL; ++j) {
+        const int g = lane + 64 * j;
+        wv[j] = (g < G) ? ld16(W + (size_t)row * row_bytes + (size_t)g * 16) : make_uint4(0, 0, 0, 0);
+      }
+    }
   }
   if (!last_block_arrived(counter, gridDim.x, &flag)) return;
 
-  // ---- last workgroup: top-k per token, softmax over the selected logits,
-  //      then the compact ascending expert list and the slot weight table.
+  // ---- last workgroup
+  __shared__ TopkScratch R;
   __shared__ int sel_id[WSX_MAX_T * WSX_MAX_K];
   __shared__ float sel_w[WSX_MAX_T * WSX_MAX_K];
   __shared__ int sel_first[WSX_MAX_T * WSX_MAX_K];
-  __shared__ int sel_rank[WSX_MAX_T * WSX_MAX_K];
   __shared__ float sw_tab[WSX_MAX_T * WSX_MAX_K * WSX_MAX_T];
-  constexpr int kPerLane = WSX_MAX_E / 64;
-  for (int t = wave; t < T; t += kRouterWaves) {
-    float lv[kPerLane];
-    unsigned taken = 0;
+#pragma unroll 1
+  for (int t = 0; t < T; ++t) {
+    block_topk<P>(logits + (size_t)t * E, E, k, &R);
+    if (threadIdx.x < k) {
+      const int j0 = threadIdx.x;
+      const float top = R.rv[0];
+      float zs = 0.f, mine = 0.f;
 #pragma unroll
-    for (int m = 0; m < kPerLane; ++m) {
-      const int e = lane + 64 * m;
-      lv[m] = (e < E) ? ld_dev(logits + (size_t)t * E + e) : -INFINITY;
-    }
-    float top[WSX_MAX_K];
-    int topi[WSX_MAX_K];
-#pragma unroll
-    for (int j = 0; j < WSX_MAX_K; ++j) {
-      top[j] = -INFINITY;
-      topi[j] = 0;
-      if (j < k) {
-        float v = -INFINITY;
-        int i = 0x7FFFFFFF;
-#pragma unroll
-        for (int m = 0; m < kPerLane; ++m) {
-          const int e = lane + 64 * m;
-          if (e < E && !((taken >> m) & 1u) && better(lv[m], e, v, i)) { v = lv[m]; i = e; }
+      for (int j = 0; j < WSX_MAX_K; ++j) {
+        if (j < k) {
+          const float z = __expf(R.rv[j] - top);
+          zs += z;
+          if (j == j0) mine = z;
         }
-        wave_argmax(v, i);
-        top[j] = v;
-        topi[j] = i;
-        if ((i & 63) == lane) taken |= 1u << (i >> 6);
       }
+      const float wj = mine / zs;
+      const int id = R.rid[j0];
+      topk_ids[t * k + j0] = id;
+      topk_w[t * k + j0] = wj;
+      sel_id[t * k + j0] = id;
+      sel_w[t * k + j0] = wj;
     }
-    float zs = 0.f, zl = 0.f;
-    int il = 0;
-#pragma unroll
-    for (int j = 0; j < WSX_MAX_K; ++j) {
-      if (j < k) {
-        const float z = __expf(top[j] - top[0]);
-        zs += z;
-        if (j == lane) { zl = z; il = topi[j]; }
-      }
-    }
-    if (lane < k) {
-      const float wj = zl / zs;
-      topk_ids[t * k + lane] = il;
-      topk_w[t * k + lane] = wj;
-      sel_id[t * k + lane] = il;
-      sel_w[t * k + lane] = wj;
-    }
+    __syncthreads();
   }
-  __syncthreads();
   const int n = T * k;
   if (wave == 0) {
     int id = (lane < n) ? sel_id[lane] : 0x7FFFFFFF;
@@ -339,13 +424,12 @@ __global__ void __launch_bounds__(64 * kRouterWaves) router_topk_kernel(
       rank += (sel_first[j] && sel_id[j] < id);
       n_active += sel_first[j];
     }
-    if (lane < n) sel_rank[lane] = rank;
     if (lane == 0) expert_list[0] = n_active;
     if (lane < n && sel_first[lane]) expert_list[1 + rank] = id;
     if (lane < n) sw_tab[rank * T + lane / k] = sel_w[lane];
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < n * T; e += NT) slot_w[e] = sw_tab[e];
+  for (int e = threadIdx.x; e < n * T; e += 256) slot_w[e] = sw_tab[e];
 }
 
 // ---------------------------------------------------------------- launchers
@@ -403,17 +487,22 @@ static hipError_t launch_router_t(const void* W, int E, int K, int k, const uint
                                   float* logits, int32_t* ids, float* w, int32_t* el, float* sw, unsigned* counter,
                                   hipStream_t st) {
   const int G = K / WTraits<WT>::EPG;
-  const int gpl = (G + 15) / 16;
-  const int NG = (E + 3) / 4;
-  const int grid = (NG + kRouterWaves - 1) / kRouterWaves;
+  const int rgpl = (G + 63) / 64;
+  const int grid = (E + 3) / 4;
+  const size_t lds = (size_t)T * K * 2;
+  const bool small = E <= 512;
 #define WSX_R_CASE(N)                                                                                              \
   case N:                                                                                                          \
-    router_topk_kernel<WT, T, N><<<grid, 64 * kRouterWaves, (size_t)T * K * 2, st>>>((const uint8_t*)W, E, K, k, x, norm, u_out, \
-                                                                      logits, ids, w, el, sw, counter);            \
+    if (small)                                                                                                     \
+      router_topk_kernel<WT, T, N, 2><<<grid, 256, lds, st>>>((const uint8_t*)W, E, K, k, x, norm, u_out, logits,  \
+                                                              ids, w, el, sw, counter);                            \
+    else                                                                                                           \
+      router_topk_kernel<WT, T, N, 4><<<grid, 256, lds, st>>>((const uint8_t*)W, E, K, k, x, norm, u_out, logits,  \
+                                                              ids, w, el, sw, counter);                            \
     break;
-  switch (gpl) {
+  switch (rgpl) {
     WSX_R_CASE(1) WSX_R_CASE(2) WSX_R_CASE(4) WSX_R_CASE(5) WSX_R_CASE(8) WSX_R_CASE(10) WSX_R_CASE(16)
-    WSX_R_CASE(20) WSX_R_CASE(32) WSX_R_CASE(40)
+    WSX_R_CASE(32)
     default: return hipErrorInvalidValue;
   }
 #undef WSX_R_CASE
@@ -423,9 +512,8 @@ static hipError_t launch_router_t(const void* W, int E, int K, int k, const uint
 bool router_shape_supported(int router_dtype, int K) {
   const int epg = router_dtype == WSX_DTYPE_F32 ? 4 : 8;
   if (K % 32 != 0 || K > kMaxK) return false;
-  const int gpl = (K / epg + 15) / 16;
-  return gpl == 1 || gpl == 2 || gpl == 4 || gpl == 5 || gpl == 8 || gpl == 10 || gpl == 16 || gpl == 20 ||
-         gpl == 32 || gpl == 40;
+  const int rgpl = (K / epg + 63) / 64;
+  return rgpl == 1 || rgpl == 2 || rgpl == 4 || rgpl == 5 || rgpl == 8 || rgpl == 10 || rgpl == 16 || rgpl == 32;
 }
 
 hipError_t launch_router(int router_dtype, const void* W, int E, int K, int k, const uint16_t* x, int T, int norm,

@@ -235,6 +235,147 @@ __global__ void __launch_bounds__(256) moe_down_kernel(int H, int I, int E, int 
   }
 }
 
+// ---------------------------------------------------------------- down for several tokens
+
+// Down + weighted combine + residual for T >= 2 tokens.  Workgroup (tile, g)
+// owns rows n0 .. n0+31 of y for the slots 4g .. 4g+3, one slot per wavefront.
+// Each wavefront stages its slot's [T][I] activations in LDS once (32-value
+// blocks at a 36-float stride, so the eight block columns a load touches fall
+// in distinct banks); lane (kg, rq) then takes rows n0 + 4 rq .. +3 over the MX
+// blocks kg, kg + 8, ...  The E2M1 codes are decoded already multiplied by
+// their power-of-two block scale (exact), so every product equals the
+// oracle's.  The four slot partials are summed in slot order, written as the
+// group's partial, and the last workgroup of the tile adds the groups in group
+// order and the residual, so the result never depends on timing.
+constexpr int kDnRows = 32;
+
+__device__ __forceinline__ int dpos(int i) { return (i >> 5) * 36 + (i & 31); }
+
+template <int T, int NKB>
+__global__ void __launch_bounds__(256) moe_down_grouped_kernel(
+    int H, int I, int E, int max_slots, const uint8_t* __restrict__ w2c, const uint8_t* __restrict__ w2s,
+    const uint8_t* __restrict__ sh2c, const uint8_t* __restrict__ sh2s, const int32_t* __restrict__ expert_list,
+    const float* __restrict__ slot_w, const float* __restrict__ a_in, const uint16_t* __restrict__ residual,
+    float* __restrict__ out_y, uint16_t* __restrict__ out_h, uint16_t* __restrict__ out_h2, float* part,
+    unsigned* counters) {
+  int n_active = expert_list[0];
+  n_active = n_active < 0 ? 0 : (n_active > max_slots - 1 ? max_slots - 1 : n_active);
+  const bool has_sh = sh2c != nullptr;
+  const int nslots = n_active + (has_sh ? 1 : 0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kg = lane & 7, rq = lane >> 3;
+  const int n0 = blockIdx.x * kDnRows;
+  const int g = blockIdx.y, s = 4 * g + wave;
+  const int NB = I / 32;
+  const int lstride = NB * 36;   // floats per token row in LDS
+  extern __shared__ __attribute__((aligned(16))) float as[];   // [4][T][lstride]
+  __shared__ float yw[4][T][kDnRows];
+  __shared__ int flag;
+  float* aw = as + (size_t)wave * T * lstride;
+
+  float acc[4][T];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[r][t] = 0.f;
+  const uint8_t *C = nullptr, *S = nullptr;
+  const bool active = s < nslots && slot_expert(s, n_active, has_sh, E, expert_list, w2c, w2s, sh2c, sh2s,
+                                                (size_t)H * (I / 2), (size_t)H * (I / 32), &C, &S);
+  if (active) {
+    // weights first (their latency overlaps the staging)
+    const size_t rowc = I / 2, rows = I / 32;
+    uint4 cw[NKB][4];
+    float sc[NKB][4];
+#pragma unroll
+    for (int b = 0; b < NKB; ++b) {
+      const int kb = kg + 8 * b;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = n0 + 4 * rq + r;
+        cw[b][r] = kb < NB ? ld16(C + row * rowc + (size_t)kb * 16) : make_uint4(0, 0, 0, 0);
+        sc[b][r] = kb < NB ? e8m0_to_f32(S[row * rows + kb]) : 0.f;
+      }
+    }
+    // this slot's activations -> LDS
+    const float4* src = reinterpret_cast<const float4*>(a_in + (size_t)s * T * I);
+    for (int q = lane; q < T * I / 4; q += 64) {
+      const int t = (4 * q) / I, i = (4 * q) % I;
+      *reinterpret_cast<float4*>(aw + t * lstride + dpos(i)) = src[q];
+    }
+#pragma unroll
+    for (int b = 0; b < NKB; ++b) {
+      const int kb = kg + 8 * b;
+      if (kb >= NB) continue;
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        float av[T][8];
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const float4* ap = reinterpret_cast<const float4*>(aw + t * lstride + kb * 36 + c4 * 8);
+          const float4 v0 = ap[0], v1 = ap[1];
+          av[t][0] = v0.x; av[t][1] = v0.y; av[t][2] = v0.z; av[t][3] = v0.w;
+          av[t][4] = v1.x; av[t][5] = v1.y; av[t][6] = v1.z; av[t][7] = v1.w;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t wd = c4 == 0 ? cw[b][r].x : c4 == 1 ? cw[b][r].y : c4 == 2 ? cw[b][r].z : cw[b][r].w;
+          const f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc[b][r], 0);
+          const f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc[b][r], 1);
+          const f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc[b][r], 2);
+          const f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc[b][r], 3);
+#pragma unroll
+          for (int t = 0; t < T; ++t) {
+            float v = acc[r][t];
+            v = fmaf(p0.x, av[t][0], v);
+            v = fmaf(p0.y, av[t][1], v);
+            v = fmaf(p1.x, av[t][2], v);
+            v = fmaf(p1.y, av[t][3], v);
+            v = fmaf(p2.x, av[t][4], v);
+            v = fmaf(p2.y, av[t][5], v);
+            v = fmaf(p3.x, av[t][6], v);
+            v = fmaf(p3.y, av[t][7], v);
+            acc[r][t] = v;
+          }
+        }
+      }
+    }
+    float wt[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) wt[t] = (s < n_active) ? slot_w[s * T + t] : 1.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int t = 0; t < T; ++t) acc[r][t] *= wt[t];
+  }
+  // sum over the 8 lanes of a row group (fixed DPP tree), one slot per wavefront
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const float v = sum8(acc[r][t]);
+      if (kg == 0) yw[wave][t][4 * rq + r] = v;
+    }
+  __syncthreads();
+  if (threadIdx.x < kDnRows * T) {
+    const int t = threadIdx.x / kDnRows, rr = threadIdx.x % kDnRows;
+    const float v = ((yw[0][t][rr] + yw[1][t][rr]) + yw[2][t][rr]) + yw[3][t][rr];
+    st_dev(part + ((size_t)g * T + t) * H + n0 + rr, v);
+  }
+  if (!last_block_arrived(counters + blockIdx.x * 16, gridDim.y, &flag)) return;
+  if (threadIdx.x < kDnRows * T) {
+    const int t = threadIdx.x / kDnRows, rr = threadIdx.x % kDnRows;
+    float y = 0.f;
+    for (int gg = 0; gg < (int)gridDim.y; ++gg) y += ld_dev(part + ((size_t)gg * T + t) * H + n0 + rr);
+    const size_t o = (size_t)t * H + n0 + rr;
+    if (out_y) out_y[o] = y;
+    if (residual) {
+      const uint16_t h = f32_to_bf16_rne(bf16_bits_to_f32(residual[o]) + y);
+      if (out_h) out_h[o] = h;
+      if (out_h2) out_h2[o] = h;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 
 bool experts_shape_supported(int H, int I) {
@@ -299,10 +440,45 @@ static hipError_t launch_down_t(int H, int I, int E, int max_slots, const uint8_
   return hipGetLastError();
 }
 
+int down_groups(int max_slots) { return (max_slots + 3) / 4; }
+size_t down_grouped_lds(int T, int I) { return (size_t)4 * T * (I / 32) * 36 * 4; }
+bool down_grouped_ok(int T, int H, int I) {
+  return T >= 2 && H % kDnRows == 0 && I / 32 <= 32 && down_grouped_lds(T, I) <= 64 * 1024;
+}
+
+template <int T>
+static hipError_t launch_down_grouped_t(int H, int I, int E, int max_slots, const uint8_t* w2c, const uint8_t* w2s,
+                                        const uint8_t* sh2c, const uint8_t* sh2s, const int32_t* el, const float* sw,
+                                        const float* a, const uint16_t* res, float* y, uint16_t* h, uint16_t* h2,
+                                        float* part, unsigned* counters, hipStream_t st) {
+  const int nkb = (I / 32 + 7) / 8;
+  dim3 grid(H / kDnRows, down_groups(max_slots));
+  const size_t lds = down_grouped_lds(T, I);
+#define WSX_DG_CASE(N)                                                                                        \
+  case N:                                                                                                     \
+    moe_down_grouped_kernel<T, N><<<grid, 256, lds, st>>>(H, I, E, max_slots, w2c, w2s, sh2c, sh2s, el, sw, a, \
+                                                          res, y, h, h2, part, counters);                      \
+    break;
+  switch (nkb) {
+    WSX_DG_CASE(1) WSX_DG_CASE(2) WSX_DG_CASE(3) WSX_DG_CASE(4)
+    default: return hipErrorInvalidValue;
+  }
+#undef WSX_DG_CASE
+  return hipGetLastError();
+}
+
 hipError_t launch_down(int T, int H, int I, int E, int k, const uint8_t* w2c, const uint8_t* w2s,
                        const uint8_t* sh2c, const uint8_t* sh2s, const int32_t* el, const float* sw, const float* a,
-                       const uint16_t* res, float* y, uint16_t* h, uint16_t* h2, hipStream_t st) {
+                       const uint16_t* res, float* y, uint16_t* h, uint16_t* h2, float* part, unsigned* counters,
+                       hipStream_t st) {
   const int max_slots = T * k + 1;
+  if (part && counters && down_grouped_ok(T, H, I)) {
+    switch (T) {
+      case 2: return launch_down_grouped_t<2>(H, I, E, max_slots, w2c, w2s, sh2c, sh2s, el, sw, a, res, y, h, h2, part, counters, st);
+      case 3: return launch_down_grouped_t<3>(H, I, E, max_slots, w2c, w2s, sh2c, sh2s, el, sw, a, res, y, h, h2, part, counters, st);
+      case 4: return launch_down_grouped_t<4>(H, I, E, max_slots, w2c, w2s, sh2c, sh2s, el, sw, a, res, y, h, h2, part, counters, st);
+    }
+  }
   const bool alds = (size_t)max_slots * T * I * 4 <= kDownLdsLimit;
 #define WSX_DT(TV)                                                                                           \
   case TV:                                                                                                   \

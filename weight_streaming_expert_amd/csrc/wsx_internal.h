@@ -32,7 +32,12 @@ hipError_t launch_gateup(const uint16_t* x, int T, int H, int I, int E, int k, c
                          float* a, hipStream_t st);
 hipError_t launch_down(int T, int H, int I, int E, int k, const uint8_t* w2c, const uint8_t* w2s,
                        const uint8_t* sh2c, const uint8_t* sh2s, const int32_t* el, const float* sw, const float* a,
-                       const uint16_t* res, float* y, uint16_t* h, uint16_t* h2, hipStream_t st);
+                       const uint16_t* res, float* y, uint16_t* h, uint16_t* h2, float* part, unsigned* counters,
+                       hipStream_t st);
+// The grouped down kernel for several tokens: slot groups per row tile, the
+// bytes of its partial sums ([groups][T][H] fp32) and its per-tile counters.
+int down_groups(int max_slots);
+bool down_grouped_ok(int T, int H, int I);
 
 // decode_step.hip: the whole 1-token decode step in one launch
 bool fused_step_supported(int T, int router_dtype, bool has_shared, int H, int I, int E, int k);
