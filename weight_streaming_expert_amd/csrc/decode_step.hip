@@ -75,7 +75,6 @@ struct FusedBufs {
   void* ctl;                 // Ctl
   unsigned* group_counter;   // [n_groups], 64-byte stride
   uint2* hx;                 // [kCopiesH][2][H/2] (bf16 pair, tag); h_l lives in [.][l & 1] (l >= 1)
-  uint2* ssx;                // [kCopiesH][2][H/8] (sum of squares of 8 rows of h_l, tag), beside hx
   uint2* lg;                 // [kCopiesLg][E] (logit, tag) of the current layer
   uint2* a;                  // [kCopiesA][nslot][I] (activation, tag) of the current layer
   uint4* hpart;              // [n_head] (value, index, tag, -)
@@ -133,9 +132,6 @@ __device__ __forceinline__ int apos(int s, int i, int I) { return s * (I / 32) *
 __device__ __forceinline__ uint2* hx_buf(const FusedStepArgs& A, int l, int c) {
   return A.b.hx + ((size_t)c * 2 + (l & 1)) * (A.H / 2);
 }
-__device__ __forceinline__ uint2* ss_buf(const FusedStepArgs& A, int l, int c) {
-  return A.b.ssx + ((size_t)c * 2 + (l & 1)) * (A.H / kDRows);
-}
 __device__ __forceinline__ uint2* lg_buf(const FusedStepArgs& A, int c) { return A.b.lg + (size_t)c * A.E; }
 __device__ __forceinline__ uint2* a_buf(const FusedStepArgs& A, int c) { return A.b.a + (size_t)c * A.nslot * A.I; }
 __device__ __forceinline__ int my_copy(int copies) { return (int)(blockIdx.x % copies); }
@@ -174,30 +170,17 @@ __device__ __forceinline__ void sleep_on_tag(const FusedStepArgs& A, const uint2
   }
 }
 
-// Each wavefront derives the RMS scale r = 1/sqrt(mean(h^2) + 1e-6) itself
-// from the published per-tile sums of squares (SPL 16-byte chunks of two
-// partials per lane, chunk q = lane + 64 i), summed in one fixed order, so
-// every wavefront of every workgroup gets bit-identical r.
-template <int SPL>
-__device__ __forceinline__ float wave_rscale(const uint4 (&sp)[SPL], int H) {
-  float ps = 0.f;
-#pragma unroll
-  for (int i = 0; i < SPL; ++i) ps += __uint_as_float(sp[i].x) + __uint_as_float(sp[i].z);
-  const float total = wave_sum_dpp(ps);
-  return 1.0f / sqrtf(total / (float)H + 1e-6f);
-}
-
-// u_l = RNE_bf16(h_l * r) into LDS (layout Lay), once every pair of h_l and
-// every partial sum of squares carries `tag`.  Each wavefront polls its share
-// of h (QPT 16-byte chunks per lane, chunk q = thread + 256 i) and all the
-// partials, without workgroup barriers; one barrier follows.
-template <int QPT, int SPL, class Lay>
-__device__ __forceinline__ void wait_u(const FusedStepArgs& A, int l, unsigned tag, uint16_t* xs) {
-  const int lane = threadIdx.x & 63;
-  const int nq = A.H / 4, nsq = A.H / kDRows / 2;
+// u_l = RNE_bf16(h_l * r) into LDS (layout Lay), r = 1/sqrt(mean(h_l^2) +
+// 1e-6), once every pair of h_l carries `tag`.  Each thread polls QPT 16-byte
+// chunks (two tagged bf16 pairs each; chunk q = thread + 256 i).  The sum of
+// squares is formed from the same values in one fixed order (the thread's
+// chunks, the DPP wavefront sum, then the four wavefronts in order), so every
+// workgroup that needs u_l derives the same r and the same u_l.
+template <int QPT, class Lay>
+__device__ __forceinline__ void wait_u(const FusedStepArgs& A, int l, unsigned tag, uint16_t* xs, float* red) {
+  const int nq = A.H / 4;
   const uint2* hxl = hx_buf(A, l, my_copy(kCopiesH));
-  const uint2* ssl = ss_buf(A, l, my_copy(kCopiesH));
-  uint4 v[QPT], sp[SPL];
+  uint4 v[QPT];
   for (int it = 0;; ++it) {
     int ok = 1;
 #pragma unroll
@@ -209,20 +192,25 @@ __device__ __forceinline__ void wait_u(const FusedStepArgs& A, int l, unsigned t
         ok &= (v[i].y == tag) & (v[i].w == tag);
       }
     }
-#pragma unroll
-    for (int i = 0; i < SPL; ++i) {
-      const int q = lane + 64 * i;
-      sp[i] = make_uint4(0, 0, 0, 0);
-      if (q < nsq) {
-        sp[i] = ld_coh16(ssl, (uint32_t)q * 16);
-        ok &= (sp[i].y == tag) & (sp[i].w == tag);
-      }
-    }
     if (__all(ok)) break;
     if (wave_should_bail(A, it)) break;
     __builtin_amdgcn_s_sleep(1);
   }
-  const float r = wave_rscale<SPL>(sp, A.H);
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const float a = bf16_bits_to_f32(v[i].x & 0xFFFFu), b = bf16_bits_to_f32(v[i].x >> 16);
+    const float c = bf16_bits_to_f32(v[i].z & 0xFFFFu), d = bf16_bits_to_f32(v[i].z >> 16);
+    ss = fmaf(a, a, ss);
+    ss = fmaf(b, b, ss);
+    ss = fmaf(c, c, ss);
+    ss = fmaf(d, d, ss);
+  }
+  ss = wave_sum_dpp(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float total = ((red[0] + red[1]) + red[2]) + red[3];
+  const float r = 1.0f / sqrtf(total / (float)A.H + 1e-6f);
 #pragma unroll
   for (int i = 0; i < QPT; ++i) {
     const int q = threadIdx.x + NT * i;
@@ -260,86 +248,16 @@ __device__ __forceinline__ void load_h_input(const uint16_t* h, int H, uint16_t*
 template <class Lay>
 __device__ __forceinline__ void rms_norm_inplace(uint16_t* xs, int H, float* red);
 
-// u_l for layer l into LDS: from the kernel input (with a workgroup reduction
-// for the scale) for l = 0, else from the tagged stream and its partials.
-template <int QPT, int SPL, class Lay>
+// u_l for layer l into LDS: from the kernel input for l = 0, else from the
+// tagged stream; either way with a workgroup reduction for the scale.
+template <int QPT, class Lay>
 __device__ __forceinline__ void get_u(const FusedStepArgs& A, int l, unsigned base, uint16_t* xs, float* red) {
   if (l == 0) {
     load_h_input<Lay>(A.h_in, A.H, xs);
     rms_norm_inplace<Lay>(xs, A.H, red);
   } else {
-    wait_u<QPT, SPL, Lay>(A, l, base + l - 1, xs);
+    wait_u<QPT, Lay>(A, l, base + l - 1, xs, red);
   }
-}
-
-// The same when h_l is known to be complete already: the loads are issued
-// now (before the caller's weight loads, so their data arrives first) and
-// committed to LDS later; a tag mismatch can only mean a broken step and
-// raises the error word.
-template <int QPT, int SPL>
-struct HRegs {
-  uint4 v[QPT];
-  uint4 sp[SPL];
-};
-
-template <int QPT, int SPL>
-__device__ __forceinline__ void h_issue(const FusedStepArgs& A, int l, HRegs<QPT, SPL>& r) {
-  const int lane = threadIdx.x & 63;
-  const uint2* src = hx_buf(A, l, my_copy(kCopiesH));
-  const uint2* ssl = ss_buf(A, l, my_copy(kCopiesH));
-#pragma unroll
-  for (int i = 0; i < QPT; ++i) {
-    const int q = threadIdx.x + NT * i;
-    r.v[i] = make_uint4(0, 0, 0, 0);
-    if (l == 0) {
-      if (q < A.H / 8) r.v[i] = ld16(A.h_in + (size_t)q * 8);
-    } else {
-      if (q < A.H / 4) r.v[i] = ld_coh16(src, (uint32_t)q * 16);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < SPL; ++i) {
-    const int q = lane + 64 * i;
-    r.sp[i] = make_uint4(0, 0, 0, 0);
-    if (l > 0 && q < A.H / kDRows / 2) r.sp[i] = ld_coh16(ssl, (uint32_t)q * 16);
-  }
-}
-
-// Commits the loads of h_issue as u_l in LDS (layout Lay).
-template <int QPT, int SPL, class Lay>
-__device__ __forceinline__ void h_commit(const FusedStepArgs& A, int l, unsigned base, const HRegs<QPT, SPL>& r,
-                                         uint16_t* xs, float* red) {
-  if (l == 0) {
-#pragma unroll
-    for (int i = 0; i < QPT; ++i) {
-      const int q = threadIdx.x + NT * i;
-      if (q < A.H / 8) *reinterpret_cast<uint4*>(xs + Lay::pos(8 * q)) = r.v[i];
-    }
-    __syncthreads();
-    rms_norm_inplace<Lay>(xs, A.H, red);
-    return;
-  }
-  const int lane = threadIdx.x & 63;
-  const unsigned tag = base + l - 1;
-  int bad = 0;
-#pragma unroll
-  for (int i = 0; i < SPL; ++i)
-    if (lane + 64 * i < A.H / kDRows / 2) bad |= (r.sp[i].y != tag) | (r.sp[i].w != tag);
-  const float sc = wave_rscale<SPL>(r.sp, A.H);
-#pragma unroll
-  for (int i = 0; i < QPT; ++i) {
-    const int q = threadIdx.x + NT * i;
-    if (q < A.H / 4) {
-      bad |= (r.v[i].y != tag) | (r.v[i].w != tag);
-      const uint32_t a = f32_to_bf16_rne(bf16_bits_to_f32(r.v[i].x & 0xFFFFu) * sc);
-      const uint32_t b = f32_to_bf16_rne(bf16_bits_to_f32(r.v[i].x >> 16) * sc);
-      const uint32_t c = f32_to_bf16_rne(bf16_bits_to_f32(r.v[i].z & 0xFFFFu) * sc);
-      const uint32_t d = f32_to_bf16_rne(bf16_bits_to_f32(r.v[i].z >> 16) * sc);
-      *reinterpret_cast<uint2*>(xs + Lay::pos(4 * q)) = make_uint2(a | (b << 16), c | (d << 16));
-    }
-  }
-  if (bad) raise_err(A);
-  __syncthreads();
 }
 
 // u = RNE_bf16(h / sqrt(mean(h^2) + 1e-6)) in place.  The sum of squares has
@@ -522,7 +440,7 @@ __device__ __forceinline__ void gateup_load(const uint8_t* C, const uint8_t* S, 
 // pairs at a_slot[i].
 template <int NJ>
 __device__ __forceinline__ void gateup_compute(const GateUpRegs<NJ>& g, const uint32_t* xs32, int H, int i0,
-                                               uint2* a_slot, size_t a_copy_stride, unsigned tag) {
+                                               uint2* a_region, int slot_off, int copy_stride, unsigned tag) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane >> 4, c = lane & 15;
   const int NB = H / 32;
@@ -546,9 +464,11 @@ __device__ __forceinline__ void gateup_compute(const GateUpRegs<NJ>& g, const ui
     const float sum = sum16(acc);
     const float up = __shfl_xor(sum, 32);
     const int ri = i0 + 4 * wave + 2 * st + (r & 1);
-    // lanes c < kCopiesA of the two gate rows each publish one copy
+    // lanes c < kCopiesA of the two gate rows each publish copy c: one store
+    // from the region's base, the copy and slot in the offset
     if (r < 2 && c < kCopiesA)
-      st_coh8(a_slot + (size_t)c * a_copy_stride, (uint32_t)ri * 8, make_uint2(__float_as_uint(silu(sum) * up), tag));
+      st_coh8(a_region, (uint32_t)(c * copy_stride + slot_off + ri) * 8,
+              make_uint2(__float_as_uint(silu(sum) * up), tag));
   }
 }
 
@@ -699,7 +619,7 @@ __device__ __forceinline__ void wave_wait_routed(const FusedStepArgs& A, unsigne
 
 // R: 8 router rows of layer l (RB-byte elements: 2 = bf16, 4 = fp32); 32 lanes
 // per row, 16-byte granules c, c+32, ...
-template <int RJ, int QPT, int SPL, int RB>
+template <int RJ, int QPT, int RB>
 __device__ __forceinline__ void role_router(const FusedStepArgs& A, int l, int r, unsigned base, uint16_t* xs,
                                             float* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -719,7 +639,7 @@ __device__ __forceinline__ void role_router(const FusedStepArgs& A, int l, int r
   // sleep on it first
   if (l > 0 && threadIdx.x == 0)
     sleep_on_tag(A, a_buf(A, my_copy(kCopiesA)), (A.k - 1) * A.I + A.I - 1, base + l - 1);
-  get_u<QPT, SPL, LayPlain>(A, l, base, xs, red);
+  get_u<QPT, LayPlain>(A, l, base, xs, red);
   if (l == 0 && r == 0 && A.h_trace)
     for (int i = threadIdx.x; i < H; i += NT) A.h_trace[i] = A.h_in[i];
   if (r == 0 && A.u_trace)
@@ -738,15 +658,15 @@ __device__ __forceinline__ void role_router(const FusedStepArgs& A, int l, int r
   acc = sum16(acc);
   const float r0 = readlane_f(acc, 0) + readlane_f(acc, 16);
   const float r1 = readlane_f(acc, 32) + readlane_f(acc, 48);
-  if (lane < kCopiesLg) {   // lane c publishes copy c
-    const int row0 = r * kRRows + 2 * wave;
-    st_coh16(lg_buf(A, lane), (uint32_t)row0 * 8,
+  // lane c publishes copy c: one store from the region's base, the copy in the offset
+  const int row0 = r * kRRows + 2 * wave;
+  if (lane < kCopiesLg)
+    st_coh16(A.b.lg, (uint32_t)(lane * A.E + row0) * 8,
              make_uint4(__float_as_uint(r0), base + l, __float_as_uint(r1), base + l));
-  }
 }
 
 // S: 16 intermediate values of the shared expert of layer l.
-template <int NJ, int QPT, int SPL>
+template <int NJ, int QPT>
 __device__ __forceinline__ void role_shared_gateup(const FusedStepArgs& A, int l, int t, unsigned base, uint16_t* xs,
                                                    float* red) {
   const int H = A.H, I = A.I;
@@ -754,13 +674,13 @@ __device__ __forceinline__ void role_shared_gateup(const FusedStepArgs& A, int l
   gateup_load<NJ>(A.sh13c + (size_t)l * 2 * I * (H / 2), A.sh13s + (size_t)l * 2 * I * (H / 32), H, I, t * kGRows, g);
   issue_here();
   if (l > 0 && threadIdx.x == 0) sleep_on_tag(A, a_buf(A, my_copy(kCopiesA)), (A.k - 1) * I + I - 1, base + l - 1);
-  get_u<QPT, SPL, LayMX>(A, l, base, xs, red);
-  gateup_compute<NJ>(g, reinterpret_cast<const uint32_t*>(xs), H, t * kGRows, A.b.a + (size_t)A.k * I,
-                     (size_t)A.nslot * I, base + l);
+  get_u<QPT, LayMX>(A, l, base, xs, red);
+  gateup_compute<NJ>(g, reinterpret_cast<const uint32_t*>(xs), H, t * kGRows, A.b.a, A.k * I, A.nslot * I,
+                     base + l);
 }
 
 // G: 16 intermediate values of routed slot s of layer l.
-template <int NJ, int QPT, int SPL>
+template <int NJ, int QPT>
 __device__ __forceinline__ void role_routed_gateup(const FusedStepArgs& A, int l, int s, int t, unsigned base,
                                                    uint16_t* xs, float* red, Routing* R) {
   const int H = A.H, I = A.I;
@@ -768,15 +688,15 @@ __device__ __forceinline__ void role_routed_gateup(const FusedStepArgs& A, int l
   // routing can be: sleep on it, normalize it, then wait for the routing
   if (l > 0 && threadIdx.x == 0) sleep_on_tag(A, hx_buf(A, l, my_copy(kCopiesH)), H / 2 - 1, base + l - 1);
   __syncthreads();
-  get_u<QPT, SPL, LayMX>(A, l, base, xs, red);
+  get_u<QPT, LayMX>(A, l, base, xs, red);
   block_route(A, base + l, R);
   // clamped: after a failed wait the routing is garbage, but reads stay in bounds
   const int e = min(max(R->sid[s], 0), A.E - 1);
   GateUpRegs<NJ> g;
   const size_t c13 = (size_t)2 * I * (H / 2), s13 = (size_t)2 * I * (H / 32);
   gateup_load<NJ>(A.w13c + ((size_t)l * A.E + e) * c13, A.w13s + ((size_t)l * A.E + e) * s13, H, I, t * kGRows, g);
-  gateup_compute<NJ>(g, reinterpret_cast<const uint32_t*>(xs), H, t * kGRows, A.b.a + (size_t)s * I,
-                     (size_t)A.nslot * I, base + l);
+  gateup_compute<NJ>(g, reinterpret_cast<const uint32_t*>(xs), H, t * kGRows, A.b.a, s * I, A.nslot * I,
+                     base + l);
 }
 
 // D: 8 output rows of layer l over every slot, the weighted combine, the
@@ -852,36 +772,20 @@ __device__ __forceinline__ void role_down(const FusedStepArgs& A, int l, int d, 
   acc = sum8(acc);
   if ((lane & 7) == 0) part[wave * kDRows + (lane >> 3)] = acc;
   __syncthreads();
-  if (threadIdx.x < kDRows / 2 * kCopiesH) {   // thread (copy c, pair q)
-    const int q = threadIdx.x % (kDRows / 2), cpy = threadIdx.x / (kDRows / 2);
-    uint32_t hb[2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int rr = 2 * q + m;
-      const float y = ((part[rr] + part[kDRows + rr]) + part[2 * kDRows + rr]) + part[3 * kDRows + rr];
-      hb[m] = f32_to_bf16_rne(part[4 * kDRows + rr] + y);
-    }
-    const int n = n0 + 2 * q;
-    st_coh8(hx_buf(A, l + 1, cpy), (uint32_t)(n >> 1) * 8, make_uint2(hb[0] | (hb[1] << 16), tag));
-    if (cpy == 0 && A.h_trace) {
-      A.h_trace[(size_t)(l + 1) * H + n] = (uint16_t)hb[0];
-      A.h_trace[(size_t)(l + 1) * H + n + 1] = (uint16_t)hb[1];
-    }
-    if (cpy == 0 && l == A.L - 1) {
-      A.h_out[n] = (uint16_t)hb[0];
-      A.h_out[n + 1] = (uint16_t)hb[1];
-    }
-  }
-  if (threadIdx.x < kCopiesH) {
-    // the tile's sum of squares of h_{l+1} (as rounded to bf16), rows in order
-    float ss = 0.f;
-#pragma unroll
-    for (int rr = 0; rr < kDRows; ++rr) {
-      const float y = ((part[rr] + part[kDRows + rr]) + part[2 * kDRows + rr]) + part[3 * kDRows + rr];
-      const float hv = bf16_bits_to_f32(f32_to_bf16_rne(part[4 * kDRows + rr] + y));
-      ss = fmaf(hv, hv, ss);
-    }
-    st_coh8(ss_buf(A, l + 1, threadIdx.x), (uint32_t)d * 8, make_uint2(__float_as_uint(ss), tag));
+  if (threadIdx.x < 64) {
+    // wavefront 0, lane (copy c = lane / 8, row rr = lane % 8): every lane
+    // forms its row of h_{l+1}; the even lanes publish the row pair of their copy
+    const int rr = lane & 7, cpy = lane >> 3;
+    const float y = ((part[rr] + part[kDRows + rr]) + part[2 * kDRows + rr]) + part[3 * kDRows + rr];
+    const uint32_t hb = f32_to_bf16_rne(part[4 * kDRows + rr] + y);
+    const uint32_t hn = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hb, kQuadSwap1, 0xF, 0xF, false);
+    const int n = n0 + rr;
+    const uint2 pv = make_uint2(hb | (hn << 16), tag);
+    // one store from the region's base, the copy in the offset
+    if ((rr & 1) == 0)
+      st_coh8(A.b.hx, (uint32_t)((cpy * 2 + ((l + 1) & 1)) * (H / 2) + (n >> 1)) * 8, pv);
+    if (cpy == 0 && A.h_trace) A.h_trace[(size_t)(l + 1) * H + n] = (uint16_t)hb;
+    if (cpy == 0 && l == A.L - 1) A.h_out[n] = (uint16_t)hb;
   }
 }
 
@@ -902,7 +806,7 @@ __device__ __forceinline__ void head_load(const FusedStepArgs& A, int grp, uint4
   sc = (ok && c == 0) ? A.hs[row] : 0.f;
 }
 
-template <int HJ, int QPT, int SPL>
+template <int HJ, int QPT>
 __device__ __forceinline__ void role_head(const FusedStepArgs& A, int hb, unsigned base, uint16_t* xs, float* red,
                                           float* wv_, int* wi_, int* flag) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -916,7 +820,7 @@ __device__ __forceinline__ void role_head(const FusedStepArgs& A, int hb, unsign
   if (grp < NG) head_load<HJ>(A, grp, w, sc);
   issue_here();
   if (threadIdx.x == 0) sleep_on_tag(A, a_buf(A, my_copy(kCopiesA)), (A.k - 1) * A.I + A.I - 1, base + L - 1);
-  wait_u<QPT, SPL, LayHead>(A, L, base + L - 1, xs);
+  wait_u<QPT, LayHead>(A, L, base + L - 1, xs, red);
   if (hb == 0 && A.u_trace)
     for (int i = threadIdx.x; i < H; i += NT) A.u_trace[(size_t)L * H + i] = xs[LayHead::pos(i)];
   const uint32_t* xs32 = reinterpret_cast<const uint32_t*>(xs);
@@ -997,7 +901,7 @@ __device__ __forceinline__ void role_head(const FusedStepArgs& A, int hb, unsign
 
 }  // namespace
 
-template <int NJ, int NJD, int RJ, int HJ, int QPT, int QA, int SPL, int RB>
+template <int NJ, int NJD, int RJ, int HJ, int QPT, int QA, int RB>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) decode_step_kernel(FusedStepArgs A) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ float red[4];
@@ -1010,18 +914,18 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) de
   const unsigned base = ((unsigned)ld_dev(reinterpret_cast<const int*>(&ctl(A)->epoch)) + 1u) << 8;
   const int bid = A.block0 + (int)blockIdx.x;
   if (bid >= A.L * A.per_layer) {
-    role_head<HJ, QPT, SPL>(A, bid - A.L * A.per_layer, base, reinterpret_cast<uint16_t*>(smem), red, wv_, wi_, &flag);
+    role_head<HJ, QPT>(A, bid - A.L * A.per_layer, base, reinterpret_cast<uint16_t*>(smem), red, wv_, wi_, &flag);
     return;
   }
   const int l = bid / A.per_layer;
   int j = bid - l * A.per_layer;
-  if (j < A.nR) { role_router<RJ, QPT, SPL, RB>(A, l, j, base, reinterpret_cast<uint16_t*>(smem), red); return; }
+  if (j < A.nR) { role_router<RJ, QPT, RB>(A, l, j, base, reinterpret_cast<uint16_t*>(smem), red); return; }
   j -= A.nR;
-  if (j < A.nS) { role_shared_gateup<NJ, QPT, SPL>(A, l, j, base, reinterpret_cast<uint16_t*>(smem), red); return; }
+  if (j < A.nS) { role_shared_gateup<NJ, QPT>(A, l, j, base, reinterpret_cast<uint16_t*>(smem), red); return; }
   j -= A.nS;
   if (j < A.nG) {
     const int tiles = A.I / kGRows;
-    role_routed_gateup<NJ, QPT, SPL>(A, l, j / tiles, j % tiles, base, reinterpret_cast<uint16_t*>(smem), red,
+    role_routed_gateup<NJ, QPT>(A, l, j / tiles, j % tiles, base, reinterpret_cast<uint16_t*>(smem), red,
                                          &R);
     return;
   }
@@ -1034,7 +938,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) de
 namespace {
 
 struct Shape {
-  int NJ, NJD, RJ, HJ, QPT, QA, SPL;
+  int NJ, NJD, RJ, HJ, QPT, QA;
 };
 
 Shape fused_shape(int H, int I, int router_bytes) {
@@ -1045,21 +949,20 @@ Shape fused_shape(int H, int I, int router_bytes) {
   s.HJ = (H / 16 + 15) / 16;
   s.QPT = (H / 4 + NT - 1) / NT;
   s.QA = (I / 2 + 63) / 64;
-  s.SPL = (H / kDRows / 2 + 63) / 64;
   return s;
 }
 
 bool is_ling(const Shape& s) {
-  return s.NJ == 5 && s.NJD == 3 && s.RJ == 10 && s.HJ == 10 && s.QPT == 3 && s.QA == 6 && s.SPL == 3;
+  return s.NJ == 5 && s.NJD == 3 && s.RJ == 10 && s.HJ == 10 && s.QPT == 3 && s.QA == 6;
 }
 bool is_tiny(const Shape& s) {
-  return s.NJ == 1 && s.NJD == 1 && s.RJ == 2 && s.HJ == 1 && s.QPT == 1 && s.QA == 1 && s.SPL == 1;
+  return s.NJ == 1 && s.NJD == 1 && s.RJ == 2 && s.HJ == 1 && s.QPT == 1 && s.QA == 1;
 }
 
 inline size_t al(size_t n) { return (n + 255) & ~(size_t)255; }
 
 struct FusedLayout {
-  size_t ctl, gcnt, hx, ssx, lg, a, hpart, gpart, total;
+  size_t ctl, gcnt, hx, lg, a, hpart, gpart, total;
   int n_head, n_groups;
 };
 
@@ -1077,8 +980,7 @@ FusedLayout fused_layout(int H, int I, int E, int k, int V) {
   f.ctl = 0;
   f.gcnt = al(f.ctl + sizeof(Ctl));
   f.hx = al(f.gcnt + (size_t)f.n_groups * 64);
-  f.ssx = al(f.hx + (size_t)kCopiesH * 2 * (H / 2) * 8);
-  f.lg = al(f.ssx + (size_t)kCopiesH * 2 * (H / kDRows) * 8);
+  f.lg = al(f.hx + (size_t)kCopiesH * 2 * (H / 2) * 8);
   f.a = al(f.lg + (size_t)kCopiesLg * E * 8);
   f.hpart = al(f.a + (size_t)kCopiesA * nslot * I * 8);
   f.gpart = al(f.hpart + (size_t)f.n_head * 16);
@@ -1123,7 +1025,6 @@ hipError_t launch_fused_step(const wsx_moe_stack* sk, const uint16_t* h_in, cons
   A.b.ctl = base + f.ctl;
   A.b.group_counter = reinterpret_cast<unsigned*>(base + f.gcnt);
   A.b.hx = reinterpret_cast<uint2*>(base + f.hx);
-  A.b.ssx = reinterpret_cast<uint2*>(base + f.ssx);
   A.b.lg = reinterpret_cast<uint2*>(base + f.lg);
   A.b.a = reinterpret_cast<uint2*>(base + f.a);
   A.b.hpart = reinterpret_cast<uint4*>(base + f.hpart);
@@ -1163,9 +1064,9 @@ hipError_t launch_fused_step(const wsx_moe_stack* sk, const uint16_t* h_in, cons
     const int grid = cuts[c + 1] - cuts[c];
     if (grid <= 0) continue;
     if (is_ling(s) && rb == 2)
-      decode_step_kernel<5, 3, 10, 10, 3, 6, 3, 2><<<grid, NT, lds, st>>>(A);
+      decode_step_kernel<5, 3, 10, 10, 3, 6, 2><<<grid, NT, lds, st>>>(A);
     else if (is_tiny(s) && rb == 4)
-      decode_step_kernel<1, 1, 2, 1, 1, 1, 1, 4><<<grid, NT, lds, st>>>(A);
+      decode_step_kernel<1, 1, 2, 1, 1, 1, 4><<<grid, NT, lds, st>>>(A);
     else
       return hipErrorInvalidValue;
     const hipError_t e = hipGetLastError();

@@ -151,6 +151,109 @@ __global__ void __launch_bounds__(256) moe_gateup_kernel(const uint16_t* __restr
   }
 }
 
+// ---------------------------------------------------------------- gate/up on the matrix cores
+
+// Gate/up + SwiGLU for T tokens with v_mfma_f32_16x16x32_bf16: workgroup
+// (i-tile, slot) computes the 16 gate rows i0.. and the 16 matching up rows
+// as two 16 x 16 tiles (rows x tokens, columns past T are zero), each
+// wavefront over a quarter of K.  The MFMA's 32-wide K slice is a
+// permutation of K: lane (row, q) supplies 8 consecutive values of MX block
+// 4 j + q of its quarter, decoded to bf16 together with the block scale (an
+// exact power-of-two product), and the token columns take the same 8
+// activations from LDS.  Products are exact; the fp32 sums differ from a
+// sequential order only by rounding.  The four quarter sums are added in
+// wavefront order.
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+__device__ __forceinline__ bf16x8_t fp4x8_to_bf16x8(uint32_t w, float scale) {
+  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+  bf16x8_t r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+template <int T, int NQ>   // NQ: groups of 4 MX blocks per wavefront quarter of K
+__global__ void __launch_bounds__(256) moe_gateup_mfma_kernel(const uint16_t* __restrict__ x, int H, int I, int E,
+                                                              int max_slots, const uint8_t* __restrict__ w13c,
+                                                              const uint8_t* __restrict__ w13s,
+                                                              const uint8_t* __restrict__ sh13c,
+                                                              const uint8_t* __restrict__ sh13s,
+                                                              const int32_t* __restrict__ expert_list,
+                                                              float* __restrict__ a_out) {
+  const int slot = blockIdx.y;
+  int n_active = expert_list[0];
+  n_active = n_active < 0 ? 0 : (n_active > max_slots - 1 ? max_slots - 1 : n_active);
+  const bool has_sh = sh13c != nullptr;
+  const int i0 = blockIdx.x * 16;
+  const uint8_t *C, *S;
+  if (!slot_expert(slot, n_active, has_sh, E, expert_list, w13c, w13s, sh13c, sh13s, (size_t)2 * I * (H / 2),
+                   (size_t)2 * I * (H / 32), &C, &S)) {
+    if (slot < n_active + (has_sh ? 1 : 0))
+      for (int i = threadIdx.x; i < 16 * T; i += 256) a_out[((size_t)slot * T + i / 16) * I + i0 + (i % 16)] = 0.f;
+    return;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = lane & 15, q = lane >> 4;
+  const int NB = H / 32;
+  const int b0 = wave * 4 * NQ;   // first MX block of this wavefront's quarter
+  const size_t rowc = H / 2, rows = H / 32;
+  // weights of both tiles first: lane (row, q) owns block b0 + 4 j + q of its row
+  uint4 cw[2][NQ];
+  float sc[2][NQ];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = h * I + i0 + row;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const int b = b0 + 4 * j + q;
+      const bool ok = b < NB;
+      cw[h][j] = ok ? ld16(C + r * rowc + (size_t)b * 16) : make_uint4(0, 0, 0, 0);
+      sc[h][j] = ok ? e8m0_to_f32(S[r * rows + b]) : 0.f;
+    }
+  }
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
+  __shared__ float red[4][2][16][T];
+  stage_to_lds<256, (T * 320 + 255) / 256>(x, xs, T * H / 8);
+  __syncthreads();
+  f32x4_t dg = {0.f, 0.f, 0.f, 0.f}, du = {0.f, 0.f, 0.f, 0.f};
+  const int col = row;   // B operand: lane (col, q)
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const int b = b0 + 4 * j + q;
+    const bool ok = b < NB;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      uint4 xv = make_uint4(0, 0, 0, 0);
+      if (col < T && ok) xv = *reinterpret_cast<const uint4*>(xs + (size_t)col * H + b * 32 + m * 8);
+      const bf16x8_t bx = __builtin_bit_cast(bf16x8_t, xv);
+      const uint32_t wg = m == 0 ? cw[0][j].x : m == 1 ? cw[0][j].y : m == 2 ? cw[0][j].z : cw[0][j].w;
+      const uint32_t wu = m == 0 ? cw[1][j].x : m == 1 ? cw[1][j].y : m == 2 ? cw[1][j].z : cw[1][j].w;
+      dg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4x8_to_bf16x8(wg, sc[0][j]), bx, dg, 0, 0, 0);
+      du = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4x8_to_bf16x8(wu, sc[1][j]), bx, du, 0, 0, 0);
+    }
+  }
+  // D: lane (col, q) holds rows 4 q .. 4 q + 3 of column col
+  if (col < T) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      red[wave][0][4 * q + r][col] = dg[r];
+      red[wave][1][4 * q + r][col] = du[r];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 16 * T) {
+    const int rr = threadIdx.x % 16, t = threadIdx.x / 16;
+    const float g = ((red[0][0][rr][t] + red[1][0][rr][t]) + red[2][0][rr][t]) + red[3][0][rr][t];
+    const float u = ((red[0][1][rr][t] + red[1][1][rr][t]) + red[2][1][rr][t]) + red[3][1][rr][t];
+    a_out[((size_t)slot * T + t) * I + i0 + rr] = silu(g) * u;
+  }
+}
+
 // ---------------------------------------------------------------- down + combine + residual
 
 template <int T, int NJD, bool ALDS>
@@ -405,10 +508,36 @@ static hipError_t launch_gateup_t(const uint16_t* x, int H, int I, int E, int ma
   return hipGetLastError();
 }
 
+template <int T>
+static hipError_t launch_gateup_mfma_t(const uint16_t* x, int H, int I, int E, int max_slots, const uint8_t* w13c,
+                                       const uint8_t* w13s, const uint8_t* sh13c, const uint8_t* sh13s,
+                                       const int32_t* el, float* a, hipStream_t st) {
+  const int nq = (H / 32 + 15) / 16;   // four wavefronts x 4 NQ blocks cover H / 32
+  dim3 grid(I / 16, max_slots);
+  const size_t lds = (size_t)T * H * 2;
+#define WSX_GM_CASE(N)                                                                                           \
+  case N:                                                                                                        \
+    moe_gateup_mfma_kernel<T, N><<<grid, 256, lds, st>>>(x, H, I, E, max_slots, w13c, w13s, sh13c, sh13s, el, a); \
+    break;
+  switch (nq) {
+    WSX_GM_CASE(1) WSX_GM_CASE(2) WSX_GM_CASE(4) WSX_GM_CASE(5) WSX_GM_CASE(8) WSX_GM_CASE(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef WSX_GM_CASE
+  return hipGetLastError();
+}
+
 hipError_t launch_gateup(const uint16_t* x, int T, int H, int I, int E, int k, const uint8_t* w13c,
                          const uint8_t* w13s, const uint8_t* sh13c, const uint8_t* sh13s, const int32_t* el,
                          float* a, hipStream_t st) {
   const int max_slots = T * k + 1;
+  if (T >= 2) {
+    switch (T) {
+      case 2: return launch_gateup_mfma_t<2>(x, H, I, E, max_slots, w13c, w13s, sh13c, sh13s, el, a, st);
+      case 3: return launch_gateup_mfma_t<3>(x, H, I, E, max_slots, w13c, w13s, sh13c, sh13s, el, a, st);
+      case 4: return launch_gateup_mfma_t<4>(x, H, I, E, max_slots, w13c, w13s, sh13c, sh13s, el, a, st);
+    }
+  }
   switch (T) {
     case 1: return launch_gateup_t<1>(x, H, I, E, max_slots, w13c, w13s, sh13c, sh13s, el, a, st);
     case 2: return launch_gateup_t<2>(x, H, I, E, max_slots, w13c, w13s, sh13c, sh13s, el, a, st);
