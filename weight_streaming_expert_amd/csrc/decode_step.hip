@@ -317,12 +317,14 @@ __device__ __forceinline__ void quad_best(float& v, int& i) {
 // Number of entries of t[0..15] that rank before (v, i): larger value, then
 // lower id.
 __device__ __forceinline__ int count_better16(const RankedLogit* t, float v, int i) {
+  uint4 p[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) p[j] = *reinterpret_cast<const uint4*>(t + 2 * j);   // all reads first
   int n = 0;
 #pragma unroll
-  for (int j = 0; j < 16; j += 2) {
-    const uint4 p = *reinterpret_cast<const uint4*>(t + j);
-    n += better(__uint_as_float(p.x), (int)p.y, v, i);
-    n += better(__uint_as_float(p.z), (int)p.w, v, i);
+  for (int j = 0; j < 8; ++j) {
+    n += better(__uint_as_float(p[j].x), (int)p[j].y, v, i);
+    n += better(__uint_as_float(p[j].z), (int)p[j].w, v, i);
   }
   return n;
 }

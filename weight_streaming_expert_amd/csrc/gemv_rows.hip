@@ -291,8 +291,13 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ lrow, int E
   if (q == 0) R->grp[t >> 2] = make_float2(bv, __int_as_float(bi));
   __syncthreads();
   int rank = 0;
+  {
+    float2 gv[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) rank += rank_before(R->grp[16 * q + j], bv, bi);
+    for (int j = 0; j < 16; ++j) gv[j] = R->grp[16 * q + j];   // all reads first
+#pragma unroll
+    for (int j = 0; j < 16; ++j) rank += rank_before(gv[j], bv, bi);
+  }
   rank += dpp_int<kQuadSwap1>(rank);
   rank += dpp_int<kQuadSwap2>(rank);
   if (rank < 8) {
@@ -304,8 +309,14 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ lrow, int E
   const float2 me = R->cand[ci];
   const int mid = __float_as_int(me.y);
   int r2 = 0;
-#pragma unroll 16
-  for (int j = 0; j < CPT; ++j) r2 += rank_before(R->cand[part * CPT + j], me.x, mid);
+#pragma unroll
+  for (int j0 = 0; j0 < CPT; j0 += 16) {
+    float2 cv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) cv[j] = R->cand[part * CPT + j0 + j];   // reads of a batch first
+#pragma unroll
+    for (int j = 0; j < 16; ++j) r2 += rank_before(cv[j], me.x, mid);
+  }
   r2 += dpp_int<kQuadSwap1>(r2);
   if constexpr (TPC == 4) r2 += dpp_int<kQuadSwap2>(r2);
   if (part == 0 && r2 < k) {

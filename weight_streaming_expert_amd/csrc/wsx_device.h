@@ -172,8 +172,11 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   }
 }
 
+// (v, i) ranks before (bv, bi): larger value, then lower index.  Written
+// without short-circuit operators so it compiles to compares and mask logic,
+// never to branches.
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
+  return (v > bv) | ((v == bv) & (i < bi));
 }
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
