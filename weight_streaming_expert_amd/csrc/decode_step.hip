@@ -181,18 +181,24 @@ __device__ __forceinline__ void wait_u(const FusedStepArgs& A, int l, unsigned t
   const int nq = A.H / 4;
   const uint2* hxl = hx_buf(A, l, my_copy(kCopiesH));
   uint4 v[QPT];
+  unsigned pend = 0;   // chunks of this thread still without `tag`; each pass re-reads only those
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    v[i] = make_uint4(0, 0, 0, 0);
+    if ((int)threadIdx.x + NT * i < nq) pend |= 1u << i;
+  }
   for (int it = 0;; ++it) {
-    int ok = 1;
 #pragma unroll
     for (int i = 0; i < QPT; ++i) {
-      const int q = threadIdx.x + NT * i;
-      v[i] = make_uint4(0, 0, 0, 0);
-      if (q < nq) {
-        v[i] = ld_coh16(hxl, (uint32_t)q * 16);
-        ok &= (v[i].y == tag) & (v[i].w == tag);
+      if (pend & (1u << i)) {
+        const uint4 w = ld_coh16(hxl, (uint32_t)(threadIdx.x + NT * i) * 16);
+        if ((w.y == tag) & (w.w == tag)) {
+          v[i] = w;
+          pend &= ~(1u << i);
+        }
       }
     }
-    if (__all(ok)) break;
+    if (__all(pend == 0)) break;
     if (wave_should_bail(A, it)) break;
     __builtin_amdgcn_s_sleep(1);
   }
@@ -545,18 +551,24 @@ __device__ __forceinline__ void wave_wait_slot(const FusedStepArgs& A, int s, un
   // sleep until the slot's last tile has been written, then poll the whole slot
   if (lane == 0) sleep_on_tag(A, src, I - 1, tag);
   uint4 p[QA];
+  unsigned pend = 0;   // chunks of this lane still without `tag`; each pass re-reads only those
+#pragma unroll
+  for (int i = 0; i < QA; ++i) {
+    p[i] = make_uint4(0, 0, 0, 0);
+    if (lane + 64 * i < nq) pend |= 1u << i;
+  }
   for (int it = 0;; ++it) {
-    int ok = 1;
 #pragma unroll
     for (int i = 0; i < QA; ++i) {
-      const int q = lane + 64 * i;
-      p[i] = make_uint4(0, 0, 0, 0);
-      if (q < nq) {
-        p[i] = ld_coh16(src, (uint32_t)q * 16);
-        ok &= (p[i].y == tag) & (p[i].w == tag);
+      if (pend & (1u << i)) {
+        const uint4 w = ld_coh16(src, (uint32_t)(lane + 64 * i) * 16);
+        if ((w.y == tag) & (w.w == tag)) {
+          p[i] = w;
+          pend &= ~(1u << i);
+        }
       }
     }
-    if (__all(ok)) break;
+    if (__all(pend == 0)) break;
     if (wave_should_bail(A, it)) break;
     __builtin_amdgcn_s_sleep(1);
   }
@@ -584,22 +596,29 @@ __device__ __forceinline__ void wave_wait_routed(const FusedStepArgs& A, unsigne
   if (last < 0) return;
   if (lane == 0) sleep_on_tag(A, abuf + (size_t)last * I, I - 1, tag);
   uint4 p[MAXR][QA];
+  unsigned pend = 0;   // chunks of this lane still without `tag`; each pass re-reads only those
+#pragma unroll
+  for (int i = 0; i < MAXR; ++i)
+#pragma unroll
+    for (int j = 0; j < QA; ++j) {
+      p[i][j] = make_uint4(0, 0, 0, 0);
+      if (wave + 4 * i < k && lane + 64 * j < nq) pend |= 1u << (i * QA + j);
+    }
   for (int it = 0;; ++it) {
-    int ok = 1;
 #pragma unroll
     for (int i = 0; i < MAXR; ++i) {
-      const int s = wave + 4 * i;
 #pragma unroll
       for (int j = 0; j < QA; ++j) {
-        const int q = lane + 64 * j;
-        p[i][j] = make_uint4(0, 0, 0, 0);
-        if (s < k && q < nq) {
-          p[i][j] = ld_coh16(abuf + (size_t)s * I, (uint32_t)q * 16);
-          ok &= (p[i][j].y == tag) & (p[i][j].w == tag);
+        if (pend & (1u << (i * QA + j))) {
+          const uint4 w = ld_coh16(abuf + (size_t)(wave + 4 * i) * I, (uint32_t)(lane + 64 * j) * 16);
+          if ((w.y == tag) & (w.w == tag)) {
+            p[i][j] = w;
+            pend &= ~(1u << (i * QA + j));
+          }
         }
       }
     }
-    if (__all(ok)) break;
+    if (__all(pend == 0)) break;
     if (wave_should_bail(A, it)) break;
     __builtin_amdgcn_s_sleep(1);
   }
