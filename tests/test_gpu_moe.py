@@ -102,9 +102,25 @@ def test_router_ties_resolve_to_lowest_id(ops):
     assert list(ids[0]) == order and list(ids[1]) == order
 
 
+def test_router_ties_resolve_to_lowest_id_many_experts(ops):
+    """More than 512 experts: four logits per thread in the rank count."""
+    H, E, k = 256, 1024, 8
+    w = inputs.normal_f32((5,), (E, H), 0.02)
+    for dup in ([7, 300, 1000], [511, 512, 1023]):
+        w[dup] = w[dup[0]] + 1.0
+    x = np.full((3, H), 0x3F80, dtype=np.uint16)
+    r = ops.moe_route_topk(P.to_dev_bf16(x), P.to_dev(w), k)
+    ids = P.np_(r["topk_ids"])
+    lg = P.np_(r["logits"])
+    assert lg[0, 7] == lg[0, 300] == lg[0, 1000] and lg[0, 511] == lg[0, 512] == lg[0, 1023]
+    order = sorted(range(E), key=lambda e: (-lg[0, e], e))[:k]
+    for t in range(3):
+        assert list(ids[t]) == order
+
+
 def test_router_k_equals_e_and_k_one(ops):
     H = 64
-    for E, k in ((8, 8), (16, 1), (1024, 8)):
+    for E, k in ((8, 8), (16, 1), (1024, 8), (513, 8), (520, 3), (1000, 5)):
         w = inputs.normal_f32((6, E), (E, H), 0.05)
         x = inputs.normal_bf16((7, E), (3, H), 1.0)
         r = ops.moe_route_topk(P.to_dev_bf16(x), P.to_dev(w), k)

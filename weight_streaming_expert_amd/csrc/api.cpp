@@ -270,7 +270,8 @@ const char* wsx_status_string(wsx_status s) {
 #define WSX_STR(x) WSX_STR2(x)
 const char* wsx_build_info(void) {
   return "libwsx arch=gfx950 hip=" WSX_STR(HIP_VERSION_MAJOR) "." WSX_STR(HIP_VERSION_MINOR)
-         " kernels=router_topk<bf16|f32,T1-4>,moe_gateup<T1-4;valu-dot2>,moe_down<T1-4;valu>,"
+         " kernels=decode_step<T1;one-launch>,router_topk<bf16|f32,T1-4;rank-count>,"
+         "moe_gateup<T1;valu-dot2|T2-4;mfma-bf16>,moe_down<T1;valu|T2-4;grouped>,"
          "lm_head<fp8|bf16,T1-4>,quant_fp8";
 }
 
