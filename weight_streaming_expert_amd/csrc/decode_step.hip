@@ -548,8 +548,8 @@ __device__ __forceinline__ void wave_wait_slot(const FusedStepArgs& A, int s, un
   const int I = A.I;
   const int nq = I / 2;
   const uint2* src = a_buf(A, my_copy(kCopiesA)) + (size_t)s * I;
-  // sleep until the slot's last tile has been written, then poll the whole slot
-  if (lane == 0) sleep_on_tag(A, src, I - 1, tag);
+  // poll from the start: each pass re-reads only the chunks still missing, so
+  // most of the slot is already in registers when its last tile lands
   uint4 p[QA];
   unsigned pend = 0;   // chunks of this lane still without `tag`; each pass re-reads only those
 #pragma unroll
@@ -594,7 +594,7 @@ __device__ __forceinline__ void wave_wait_routed(const FusedStepArgs& A, unsigne
   for (int i = 0; i < MAXR; ++i)
     if (wave + 4 * i < k) last = wave + 4 * i;
   if (last < 0) return;
-  if (lane == 0) sleep_on_tag(A, abuf + (size_t)last * I, I - 1, tag);
+  // poll from the start (see wave_wait_slot)
   uint4 p[MAXR][QA];
   unsigned pend = 0;   // chunks of this lane still without `tag`; each pass re-reads only those
 #pragma unroll
@@ -759,6 +759,17 @@ __device__ __forceinline__ void role_down(const FusedStepArgs& A, int l, int d, 
     }
     part[4 * kDRows + threadIdx.x] = res;
   }
+  // the shared expert first (owned by wavefront k % 4): its activations are
+  // stored before the routing is known, so this wait overlaps the routing's
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXS; ++i) {
+    const int s = wave + 4 * i;
+    if (s == k && s < nslot) {
+      wave_wait_slot<QA>(A, s, tag, as + apos(s, 0, I));
+      acc = down_dot<NJD>(dr[i], as + apos(s, 0, I), I, 1.0f, acc);
+    }
+  }
   block_route(A, tag, R);
   if (d == 0 && threadIdx.x < k) {
     if (A.ids_trace) A.ids_trace[(size_t)l * k + threadIdx.x] = R->rid[threadIdx.x];
@@ -773,17 +784,6 @@ __device__ __forceinline__ void role_down(const FusedStepArgs& A, int l, int d, 
     }
   }
   issue_here();
-  float acc = 0.f;
-  // the shared expert first (owned by wavefront k % 4; its activations are
-  // ready early), then the routed slots
-#pragma unroll
-  for (int i = 0; i < MAXS; ++i) {
-    const int s = wave + 4 * i;
-    if (s == k && s < nslot) {
-      wave_wait_slot<QA>(A, s, tag, as + apos(s, 0, I));
-      acc = down_dot<NJD>(dr[i], as + apos(s, 0, I), I, 1.0f, acc);
-    }
-  }
   wave_wait_routed<QA, (WSX_MAX_K + 3) / 4>(A, tag, as);
 #pragma unroll
   for (int i = 0; i < MAXS; ++i) {
