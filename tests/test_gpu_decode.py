@@ -88,6 +88,45 @@ def test_ling_shape_stack_decode_step(ops, ling_stack, T):
         check_step(wl, layers, out, qh, sh, h0)
 
 
+def check_exact_ties(ids, logits):
+    """Among exactly equal logits the lower id is selected first and ranks first."""
+    for g, l in zip(np.atleast_2d(ids), np.atleast_2d(logits)):
+        for a, b in zip(g[:-1], g[1:]):
+            assert l[a] != l[b] or a < b, f"tied ids {a}, {b} out of order"
+        sel = set(int(e) for e in g)
+        for s in sel:
+            tied = np.flatnonzero(l == l[s])
+            assert all(int(e) in sel for e in tied if e < s), f"id {s} chosen over a lower tied id"
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_fused_routing_exact_ties(ops, ling_stack, T):
+    """Repeated router rows give exactly tied logits: in layer 0 row e equals row
+    e % 64, so each value has eight copies in eight different groups of eight
+    ids; in layer 1 row e equals row e - e % 2, a tied pair inside each group.
+    The fused step picks and ranks tied experts by lower id ([genai] and [sns],
+    the router's top-k; ties are ordered by lower id)."""
+    wl, layers, stack, head, qh, sh = ling_stack
+    E = wl.moe.E
+    idx = (np.arange(E) % 64, np.arange(E) - np.arange(E) % 2)
+    tied = [dict(lw, router=lw["router"][ix].copy()) for lw, ix in zip(layers, idx)]
+    r = np.stack([lw["router"] for lw in tied])
+    router = P.to_dev(r) if r.dtype == np.float32 else P.to_dev_bf16(r)
+    st = ops.MoeStackTensors(router, stack.w13_codes, stack.w13_scales, stack.w2_codes, stack.w2_scales,
+                             shared=stack.shared, k=stack.k)
+    h0 = inputs.normal_bf16((wl.seed, inputs.T_X, 7, T), (T, wl.moe.H), 1.0)
+    out = ops.moe_decode_step(P.to_dev_bf16(h0), st, head, trace=True)
+    check_step(wl, tied, out, qh, sh, h0)
+    ut, ids = P.bits(out["u_trace"]), P.np_(out["ids_trace"])
+    for l, lw in enumerate(tied):
+        ref = OM.router_logits(ut[l], P.router_values(lw["router"]))
+        check_exact_ties(ids[l], ref)
+        if l == 0:   # the eight copies of the best value fill the top k
+            for t in range(T):
+                assert np.all(ids[l][t] % 64 == ids[l][t][0] % 64)
+                assert np.all(np.diff(ids[l][t]) == 64)
+
+
 def test_decode_step_is_deterministic(ops, ling_stack):
     wl, layers, stack, head, qh, sh = ling_stack
     h0 = P.to_dev_bf16(inputs.normal_bf16((3,), (1, wl.moe.H), 1.0))

@@ -287,69 +287,76 @@ __device__ __forceinline__ void rms_norm_inplace(uint16_t* xs, int H, float* red
 
 // ---------------------------------------------------------------- routing
 
-struct RankedLogit {
-  float v;
-  int id;
-};
-struct alignas(16) Routing {
-  RankedLogit grp[kRouteGroups];   // best logit of each group of 8
-  RankedLogit cand[kRouteGroups];  // all logits of the kRouteCand best groups
-  float rv[WSX_MAX_K];     // selected logits in rank order
-  int rid[WSX_MAX_K];      // selected ids in rank order
-  float rw[WSX_MAX_K];     // routing weights in rank order
-  int sid[WSX_MAX_K];      // selected ids, ascending (slot order)
-  float sw[WSX_MAX_K];     // routing weight of each slot
-};
-
-// Afterwards (va, ia) ranks before (vb, ib): larger value, then lower id.
-__device__ __forceinline__ void cmpswap(float& va, int& ia, float& vb, int& ib) {
-  if (better(vb, ib, va, ia)) {
-    const float tv = va; va = vb; vb = tv;
-    const int ti = ia; ia = ib; ib = ti;
-  }
+// A logit's rank key: the value's bits mapped to an unsigned integer that
+// orders as the value does (-0 taken as +0), above the complement of the id.
+// A larger key ranks before: larger value, then lower id.
+using RankKey = unsigned long long;
+__device__ __forceinline__ RankKey rank_key(float v, int id) {
+  const unsigned b = __float_as_uint(v + 0.0f);
+  const unsigned o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((RankKey)o << 32) | (unsigned)~id;
 }
+__device__ __forceinline__ float key_value(RankKey key) {
+  const unsigned o = (unsigned)(key >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+__device__ __forceinline__ int key_id(RankKey key) { return (int)~(unsigned)key; }
 
 template <int CTRL>
 __device__ __forceinline__ int dpp_i(int v) { return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false); }
 
-// Keep the better of (v, i) and its partner lane's pair under quad_perm CTRL.
 template <int CTRL>
-__device__ __forceinline__ void quad_best(float& v, int& i) {
-  const float ov = dpp_f<CTRL>(v);
-  const int oi = dpp_i<CTRL>(i);
-  if (better(ov, oi, v, i)) { v = ov; i = oi; }
+__device__ __forceinline__ RankKey dpp_key(RankKey x) {
+  const unsigned lo = (unsigned)dpp_i<CTRL>((int)(unsigned)x);
+  const unsigned hi = (unsigned)dpp_i<CTRL>((int)(unsigned)(x >> 32));
+  return ((RankKey)hi << 32) | lo;
 }
 
-// Number of entries of t[0..15] that rank before (v, i): larger value, then
-// lower id.
-__device__ __forceinline__ int count_better16(const RankedLogit* t, float v, int i) {
-  uint4 p[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) p[j] = *reinterpret_cast<const uint4*>(t + 2 * j);   // all reads first
+// The routing of one layer as each wavefront of the workgroup sees it: the k
+// selected experts in rank order and in slot order (ascending ids).
+struct WaveRouting {
+  int rid[WSX_MAX_K];     // selected ids in rank order
+  float rw[WSX_MAX_K];    // routing weights in rank order
+  int sid[WSX_MAX_K];     // selected ids, ascending (slot order)
+  float sw[WSX_MAX_K];    // routing weight of each slot
+};
+struct alignas(16) Routing {
+  RankKey grp[kRouteGroups];    // best key of each group of 8
+  RankKey cand[kRouteGroups];   // all keys of the kRouteCand best groups
+  RankKey top[WSX_MAX_K];       // the k selected keys in rank order
+  WaveRouting w[NT / 64];       // one copy per wavefront, written and read by it alone
+};
+
+// Number of the 16 keys at t that rank before `me` (read in two halves: eight
+// 16-byte reads at once make the compiler spill elsewhere in the kernel).
+__device__ __forceinline__ int count_above16(const RankKey* t, RankKey me) {
   int n = 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    n += better(__uint_as_float(p[j].x), (int)p[j].y, v, i);
-    n += better(__uint_as_float(p[j].z), (int)p[j].w, v, i);
+  for (int h = 0; h < 2; ++h) {
+    ulonglong2 p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p[j] = reinterpret_cast<const ulonglong2*>(t)[4 * h + j];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) n += (int)(p[j].x > me) + (int)(p[j].y > me);
   }
   return n;
 }
 
 // Top-k routing of one layer by the whole workgroup, with no sequential
 // selection rounds ([genai] and [sns], the router: softmax over the k largest
-// of the E expert logits).  Logits rank by value, then by lower id.  Thread t
-// holds logits 2t and 2t+1 (E <= 2 NT; positions past E hold -inf), and each
-// four consecutive threads form a group of 8.  A logit whose group's best
-// logit is beaten by the best logits of k other groups is itself beaten by k
-// logits, so the top k lie in the kRouteCand (>= k) groups whose best logits
-// rank highest.  Both rankings, of the 64 group maxima and then of the 64
-// logits of those groups, count pairwise wins (16 per thread, summed over the
-// group's four threads), so every rank is found at once.  The k selected
-// logits are then normalized by a softmax taken in rank order, and the slot
-// order (ascending ids) is their rank among the selected ids.  The result is
-// left in LDS for the whole workgroup.
+// of the E expert logits).  Logits rank by value, then by lower id, through
+// their rank keys.  Thread t holds logits 2t and 2t+1 (E <= 2 NT; positions
+// past E hold -inf), and each four consecutive threads form a group of 8.  A
+// logit whose group's best logit is beaten by the best logits of k other
+// groups is itself beaten by k logits, so the top k lie in the kRouteCand
+// (>= k) groups whose best logits rank highest.  Both rankings, of the 64
+// group maxima and then of the 64 logits of those groups, count pairwise wins
+// (16 per thread, summed over the group's four threads), so every rank is
+// found at once.  Each wavefront then normalizes the k selected logits by a
+// softmax taken in rank order, finds each one's slot (its rank among the
+// selected ids) and keeps the result in its own copy of the routing.
 __device__ __forceinline__ void block_route(const FusedStepArgs& A, unsigned tag, Routing* R) {
-  const int t = threadIdx.x, q = t & 3, E = A.E, k = A.k;
+  const int t = threadIdx.x, q = t & 3, lane = t & 63, E = A.E, k = A.k;
   const int e0 = 2 * t;
   const uint2* lgc = lg_buf(A, my_copy(kCopiesLg));
   float v0 = -INFINITY, v1 = -INFINITY;
@@ -365,51 +372,56 @@ __device__ __forceinline__ void block_route(const FusedStepArgs& A, unsigned tag
     if (wave_should_bail(A, it)) break;
     __builtin_amdgcn_s_sleep(1);
   }
-  // best logit of the group (every thread of the four ends with it)
-  float bv = v0;
-  int bi = e0;
-  if (better(v1, e0 + 1, bv, bi)) { bv = v1; bi = e0 + 1; }
-  quad_best<kQuadSwap1>(bv, bi);
-  quad_best<kQuadSwap2>(bv, bi);
-  if (q == 0) R->grp[t >> 2] = RankedLogit{bv, bi};
+  const RankKey k0 = rank_key(v0, e0), k1 = rank_key(v1, e0 + 1);
+  // best key of the group (every thread of the four ends with it)
+  RankKey best = k0 > k1 ? k0 : k1;
+  RankKey o = dpp_key<kQuadSwap1>(best);
+  best = o > best ? o : best;
+  o = dpp_key<kQuadSwap2>(best);
+  best = o > best ? o : best;
+  if (q == 0) R->grp[t >> 2] = best;
   __syncthreads();
-  int rank = count_better16(R->grp + 16 * q, bv, bi);
+  int rank = count_above16(R->grp + 16 * q, best);
   rank += dpp_i<kQuadSwap1>(rank);
   rank += dpp_i<kQuadSwap2>(rank);
-  if (rank < kRouteCand) {
-    *reinterpret_cast<uint4*>(R->cand + rank * 8 + 2 * q) =
-        make_uint4(__float_as_uint(v0), (unsigned)e0, __float_as_uint(v1), (unsigned)(e0 + 1));
-  }
+  if (rank < kRouteCand) reinterpret_cast<ulonglong2*>(R->cand + rank * 8)[q] = make_ulonglong2(k0, k1);
   __syncthreads();
-  const RankedLogit me = R->cand[t >> 2];
-  rank = count_better16(R->cand + 16 * q, me.v, me.id);
+  const RankKey me = R->cand[t >> 2];
+  rank = count_above16(R->cand + 16 * q, me);
   rank += dpp_i<kQuadSwap1>(rank);
   rank += dpp_i<kQuadSwap2>(rank);
-  if (q == 0 && rank < k) {
-    R->rv[rank] = me.v;
-    R->rid[rank] = me.id;
-  }
+  if (q == 0 && rank < k) R->top[rank] = me;
   __syncthreads();
-  if (t < k) {
-    const int myid = R->rid[t];
-    const float top = R->rv[0];
-    float zs = 0.f, mine = 0.f;
-    int slot = 0;
+  // every wavefront: lane r < k takes the logit of rank r; the softmax sums in
+  // rank order, the same in every lane
+  const RankKey key = (lane < k) ? R->top[lane] : 0ull;
+  const float v = key_value(key);
+  const int id = key_id(key);
+  const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  float zs = 0.f, mine = 0.f;
+  int slot = 0;
 #pragma unroll
-    for (int j = 0; j < WSX_MAX_K; ++j) {
-      if (j < k) {
-        const float z = __expf(R->rv[j] - top);
-        zs += z;
-        if (j == t) mine = z;
-        slot += R->rid[j] < myid;
-      }
+  for (int j = 0; j < WSX_MAX_K; ++j) {
+    if (j < k) {
+      const float z = __expf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j)) - top);
+      zs += z;
+      if (j == lane) mine = z;
+      slot += __builtin_amdgcn_readlane(id, j) < id;
     }
-    const float w = mine / zs;
-    R->rw[t] = w;
-    R->sid[slot] = myid;
-    R->sw[slot] = w;
   }
-  __syncthreads();
+  if (lane < k) {
+    WaveRouting& W = R->w[t >> 6];
+    const float w = mine / zs;
+    W.rid[lane] = id;
+    W.rw[lane] = w;
+    W.sid[slot] = id;
+    W.sw[slot] = w;
+  }
+  // the wavefront reads its copy back in other lanes: LDS accesses of one
+  // wavefront complete in order, so only the compiler has to keep them so
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // ---------------------------------------------------------------- gate/up tile
@@ -712,7 +724,7 @@ __device__ __forceinline__ void role_routed_gateup(const FusedStepArgs& A, int l
   get_u<QPT, LayMX>(A, l, base, xs, red);
   block_route(A, base + l, R);
   // clamped: after a failed wait the routing is garbage, but reads stay in bounds
-  const int e = min(max(R->sid[s], 0), A.E - 1);
+  const int e = min(max(R->w[threadIdx.x >> 6].sid[s], 0), A.E - 1);
   GateUpRegs<NJ> g;
   const size_t c13 = (size_t)2 * I * (H / 2), s13 = (size_t)2 * I * (H / 32);
   gateup_load<NJ>(A.w13c + ((size_t)l * A.E + e) * c13, A.w13s + ((size_t)l * A.E + e) * s13, H, I, t * kGRows, g);
@@ -772,14 +784,14 @@ __device__ __forceinline__ void role_down(const FusedStepArgs& A, int l, int d, 
   }
   block_route(A, tag, R);
   if (d == 0 && threadIdx.x < k) {
-    if (A.ids_trace) A.ids_trace[(size_t)l * k + threadIdx.x] = R->rid[threadIdx.x];
-    if (A.w_trace) A.w_trace[(size_t)l * k + threadIdx.x] = R->rw[threadIdx.x];
+    if (A.ids_trace) A.ids_trace[(size_t)l * k + threadIdx.x] = R->w[0].rid[threadIdx.x];
+    if (A.w_trace) A.w_trace[(size_t)l * k + threadIdx.x] = R->w[0].rw[threadIdx.x];
   }
 #pragma unroll
   for (int i = 0; i < MAXS; ++i) {
     const int s = wave + 4 * i;
     if (s < k) {
-      const int e = min(max(R->sid[s], 0), E - 1);
+      const int e = min(max(R->w[wave].sid[s], 0), E - 1);
       down_load<NJD>(A.w2c + ((size_t)l * E + e) * c2, A.w2s + ((size_t)l * E + e) * s2, I, n0, dr[i]);
     }
   }
@@ -788,7 +800,7 @@ __device__ __forceinline__ void role_down(const FusedStepArgs& A, int l, int d, 
 #pragma unroll
   for (int i = 0; i < MAXS; ++i) {
     const int s = wave + 4 * i;
-    if (s < k) acc = down_dot<NJD>(dr[i], as + apos(s, 0, I), I, R->sw[s], acc);
+    if (s < k) acc = down_dot<NJD>(dr[i], as + apos(s, 0, I), I, R->w[wave].sw[s], acc);
   }
   acc = sum8(acc);
   if ((lane & 7) == 0) part[wave * kDRows + (lane >> 3)] = acc;
