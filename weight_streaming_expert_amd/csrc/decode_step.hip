@@ -285,6 +285,14 @@ __device__ __forceinline__ void rms_norm_inplace(uint16_t* xs, int H, float* red
   __syncthreads();
 }
 
+// Streamed weights are read once per step: nontemporal loads keep them from
+// displacing the exchange buffers that the workgroups poll.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // ---------------------------------------------------------------- routing
 
 // A logit's rank key: the value's bits mapped to an unsigned integer that
@@ -450,7 +458,7 @@ __device__ __forceinline__ void gateup_load(const uint8_t* C, const uint8_t* S, 
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int b = c + 16 * j;
-      g.cw[st][j] = (b < NB) ? ld16(C + row * rowc + (size_t)b * 16) : make_uint4(0, 0, 0, 0);
+      g.cw[st][j] = (b < NB) ? ld16_stream(C + row * rowc + (size_t)b * 16) : make_uint4(0, 0, 0, 0);
       g.sb[st][j] = (b < NB) ? (uint32_t)S[row * rows + b] : 127u;
     }
   }
@@ -511,7 +519,7 @@ __device__ __forceinline__ void down_load(const uint8_t* C, const uint8_t* S, in
 #pragma unroll
   for (int j = 0; j < NJD; ++j) {
     const int b = c + 8 * j;
-    d.cw[j] = (b < NB) ? ld16(C + row * rowc + (size_t)b * 16) : make_uint4(0, 0, 0, 0);
+    d.cw[j] = (b < NB) ? ld16_stream(C + row * rowc + (size_t)b * 16) : make_uint4(0, 0, 0, 0);
     d.sb[j] = (b < NB) ? (uint32_t)S[row * rows + b] : 127u;
   }
 }
@@ -665,7 +673,7 @@ __device__ __forceinline__ void role_router(const FusedStepArgs& A, int l, int r
 #pragma unroll
   for (int j = 0; j < RJ; ++j) {
     const int g = c + 32 * j;
-    wr[j] = g < G ? ld16(W + (size_t)g * 16) : make_uint4(0, 0, 0, 0);
+    wr[j] = g < G ? ld16_stream(W + (size_t)g * 16) : make_uint4(0, 0, 0, 0);
   }
   issue_here();
   // the previous layer's gate/up stage completes before its down stage can:
@@ -834,7 +842,7 @@ __device__ __forceinline__ void head_load(const FusedStepArgs& A, int grp, uint4
 #pragma unroll
   for (int j = 0; j < HJ; ++j) {
     const int g = c + 16 * j;
-    w[j] = (ok && g < G) ? ld16(A.hq + (size_t)row * A.H + (size_t)g * 16) : make_uint4(0, 0, 0, 0);
+    w[j] = (ok && g < G) ? ld16_stream(A.hq + (size_t)row * A.H + (size_t)g * 16) : make_uint4(0, 0, 0, 0);
   }
   sc = (ok && c == 0) ? A.hs[row] : 0.f;
 }
