@@ -360,11 +360,9 @@ __device__ __forceinline__ int count_above16(const RankKey* t, RankKey me) {
 // (>= k) groups whose best logits rank highest.  Both rankings, of the 64
 // group maxima and then of the 64 logits of those groups, count pairwise wins
 // (16 per thread, summed over the group's four threads), so every rank is
-// found at once.  Each wavefront then normalizes the k selected logits by a
-// softmax taken in rank order, finds each one's slot (its rank among the
-// selected ids) and keeps the result in its own copy of the routing.
-__device__ __forceinline__ void block_route(const FusedStepArgs& A, unsigned tag, Routing* R) {
-  const int t = threadIdx.x, q = t & 3, lane = t & 63, E = A.E, k = A.k;
+// found at once.  Leaves the k selected keys in rank order in R->top.
+__device__ __forceinline__ void route_topk(const FusedStepArgs& A, unsigned tag, Routing* R) {
+  const int t = threadIdx.x, q = t & 3, E = A.E, k = A.k;
   const int e0 = 2 * t;
   const uint2* lgc = lg_buf(A, my_copy(kCopiesLg));
   float v0 = -INFINITY, v1 = -INFINITY;
@@ -400,8 +398,14 @@ __device__ __forceinline__ void block_route(const FusedStepArgs& A, unsigned tag
   rank += dpp_i<kQuadSwap2>(rank);
   if (q == 0 && rank < k) R->top[rank] = me;
   __syncthreads();
-  // every wavefront: lane r < k takes the logit of rank r; the softmax sums in
-  // rank order, the same in every lane
+}
+
+// The routing weights, by every wavefront for itself: lane r < k takes the
+// logit of rank r, the softmax sums in rank order (the same in every lane),
+// and each selected expert's slot is its rank among the selected ids.  The
+// result goes to the wavefront's own copy, R->w[wavefront].
+__device__ __forceinline__ void route_weights(const FusedStepArgs& A, Routing* R) {
+  const int lane = threadIdx.x & 63, k = A.k;
   const RankKey key = (lane < k) ? R->top[lane] : 0ull;
   const float v = key_value(key);
   const int id = key_id(key);
@@ -418,7 +422,7 @@ __device__ __forceinline__ void block_route(const FusedStepArgs& A, unsigned tag
     }
   }
   if (lane < k) {
-    WaveRouting& W = R->w[t >> 6];
+    WaveRouting& W = R->w[threadIdx.x >> 6];
     const float w = mine / zs;
     W.rid[lane] = id;
     W.rw[lane] = w;
@@ -430,6 +434,19 @@ __device__ __forceinline__ void block_route(const FusedStepArgs& A, unsigned tag
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The expert of slot s (the s-th smallest selected id), by every wavefront
+// for itself, without the weights.
+__device__ __forceinline__ int route_slot_expert(const FusedStepArgs& A, const Routing* R, int s) {
+  const int lane = threadIdx.x & 63, k = A.k;
+  const int id = key_id((lane < k) ? R->top[lane] : 0ull);
+  int slot = 0;
+#pragma unroll
+  for (int j = 0; j < WSX_MAX_K; ++j)
+    if (j < k) slot += __builtin_amdgcn_readlane(id, j) < id;
+  const unsigned long long hit = __ballot((lane < k) & (slot == s));
+  return hit ? __builtin_amdgcn_readlane(id, __builtin_ctzll(hit)) : 0;
 }
 
 // ---------------------------------------------------------------- gate/up tile
@@ -730,9 +747,9 @@ __device__ __forceinline__ void role_routed_gateup(const FusedStepArgs& A, int l
   if (l > 0 && threadIdx.x == 0) sleep_on_tag(A, hx_buf(A, l, my_copy(kCopiesH)), H / 2 - 1, base + l - 1);
   __syncthreads();
   get_u<QPT, LayMX>(A, l, base, xs, red);
-  block_route(A, base + l, R);
+  route_topk(A, base + l, R);
   // clamped: after a failed wait the routing is garbage, but reads stay in bounds
-  const int e = min(max(R->w[threadIdx.x >> 6].sid[s], 0), A.E - 1);
+  const int e = min(max(route_slot_expert(A, R, s), 0), A.E - 1);
   GateUpRegs<NJ> g;
   const size_t c13 = (size_t)2 * I * (H / 2), s13 = (size_t)2 * I * (H / 32);
   gateup_load<NJ>(A.w13c + ((size_t)l * A.E + e) * c13, A.w13s + ((size_t)l * A.E + e) * s13, H, I, t * kGRows, g);
@@ -790,7 +807,8 @@ __device__ __forceinline__ void role_down(const FusedStepArgs& A, int l, int d, 
       acc = down_dot<NJD>(dr[i], as + apos(s, 0, I), I, 1.0f, acc);
     }
   }
-  block_route(A, tag, R);
+  route_topk(A, tag, R);
+  route_weights(A, R);
   if (d == 0 && threadIdx.x < k) {
     if (A.ids_trace) A.ids_trace[(size_t)l * k + threadIdx.x] = R->w[0].rid[threadIdx.x];
     if (A.w_trace) A.w_trace[(size_t)l * k + threadIdx.x] = R->w[0].rw[threadIdx.x];
