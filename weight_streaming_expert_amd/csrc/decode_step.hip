@@ -578,29 +578,27 @@ __device__ __forceinline__ float down_dot(const DownRegs<NJD>& d, const float* a
 
 // One wavefront waits until slot s's I activations carry `tag` and copies
 // them to LDS (as fp32).  QA 16-byte chunks (two pairs each) per lane cover
-// the I/2 chunks, all in flight together.
+// the I/2 chunks.
 template <int QA>
 __device__ __forceinline__ void wave_wait_slot(const FusedStepArgs& A, int s, unsigned tag, float* as_slot) {
   const int lane = threadIdx.x & 63;
   const int I = A.I;
   const int nq = I / 2;
   const uint2* src = a_buf(A, my_copy(kCopiesA)) + (size_t)s * I;
-  // poll from the start: each pass re-reads only the chunks still missing, so
-  // most of the slot is already in registers when its last tile lands
-  uint4 p[QA];
-  unsigned pend = 0;   // chunks of this lane still without `tag`; each pass re-reads only those
+  // poll from the start: each pass re-reads only the chunks still missing, and
+  // a chunk goes to LDS as soon as it arrives
+  unsigned pend = 0;   // chunks of this lane still without `tag`
 #pragma unroll
-  for (int i = 0; i < QA; ++i) {
-    p[i] = make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < QA; ++i)
     if (lane + 64 * i < nq) pend |= 1u << i;
-  }
   for (int it = 0;; ++it) {
 #pragma unroll
     for (int i = 0; i < QA; ++i) {
       if (pend & (1u << i)) {
-        const uint4 w = ld_coh16(src, (uint32_t)(lane + 64 * i) * 16);
+        const int q = lane + 64 * i;
+        const uint4 w = ld_coh16(src, (uint32_t)q * 16);
         if ((w.y == tag) & (w.w == tag)) {
-          p[i] = w;
+          *reinterpret_cast<float2*>(as_slot + apos(0, 2 * q, I)) = make_float2(__uint_as_float(w.x), __uint_as_float(w.z));
           pend &= ~(1u << i);
         }
       }
@@ -609,67 +607,63 @@ __device__ __forceinline__ void wave_wait_slot(const FusedStepArgs& A, int s, un
     if (wave_should_bail(A, it)) break;
     __builtin_amdgcn_s_sleep(1);
   }
-#pragma unroll
-  for (int i = 0; i < QA; ++i) {
-    const int q = lane + 64 * i;
-    if (q < nq) {
-      *reinterpret_cast<float2*>(as_slot + apos(0, 2 * q, I)) = make_float2(__uint_as_float(p[i].x), __uint_as_float(p[i].z));
-    }
-  }
 }
 
-// One wavefront waits for all of its routed slots (s = wave + 4 i < k) at once
-// and copies their activations to LDS.
-template <int QA, int MAXR>
-__device__ __forceinline__ void wave_wait_routed(const FusedStepArgs& A, unsigned tag, float* as) {
+// One wavefront's routed slots (s = wave + 4 i < k): it polls all of their
+// activations at once, copying each chunk to LDS (as fp32) as it arrives, and
+// takes a slot's dot product (weight sw[s]) into accs[i] as soon as every
+// chunk of that slot is in, so only the slot that arrives last is left for
+// after the gate/up stage.  Each slot keeps its own sum, so the result does
+// not depend on the order of arrival.
+template <int QA, int MAXR, int NJD, int MAXS>
+__device__ __forceinline__ void wave_routed_dots(const FusedStepArgs& A, unsigned tag, float* as,
+                                                 const DownRegs<NJD> (&dr)[MAXS], const float* sw, float (&accs)[MAXR]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int I = A.I, k = A.k;
   const int nq = I / 2;
   const uint2* abuf = a_buf(A, my_copy(kCopiesA));
-  int last = -1;
-#pragma unroll
-  for (int i = 0; i < MAXR; ++i)
-    if (wave + 4 * i < k) last = wave + 4 * i;
-  if (last < 0) return;
-  // poll from the start (see wave_wait_slot)
-  uint4 p[MAXR][QA];
   unsigned pend = 0;   // chunks of this lane still without `tag`; each pass re-reads only those
+  unsigned todo = 0;   // slots whose dot product is still to take (the same in every lane)
 #pragma unroll
-  for (int i = 0; i < MAXR; ++i)
+  for (int i = 0; i < MAXR; ++i) {
+    accs[i] = 0.f;
+    if (wave + 4 * i < k) {
+      todo |= 1u << i;
 #pragma unroll
-    for (int j = 0; j < QA; ++j) {
-      p[i][j] = make_uint4(0, 0, 0, 0);
-      if (wave + 4 * i < k && lane + 64 * j < nq) pend |= 1u << (i * QA + j);
+      for (int j = 0; j < QA; ++j)
+        if (lane + 64 * j < nq) pend |= 1u << (i * QA + j);
     }
-  for (int it = 0;; ++it) {
+  }
+  for (int it = 0; todo; ++it) {
 #pragma unroll
     for (int i = 0; i < MAXR; ++i) {
 #pragma unroll
       for (int j = 0; j < QA; ++j) {
         if (pend & (1u << (i * QA + j))) {
-          const uint4 w = ld_coh16(abuf + (size_t)(wave + 4 * i) * I, (uint32_t)(lane + 64 * j) * 16);
+          const int q = lane + 64 * j;
+          const uint4 w = ld_coh16(abuf + (size_t)(wave + 4 * i) * I, (uint32_t)q * 16);
           if ((w.y == tag) & (w.w == tag)) {
-            p[i][j] = w;
+            *reinterpret_cast<float2*>(as + apos(wave + 4 * i, 2 * q, I)) =
+                make_float2(__uint_as_float(w.x), __uint_as_float(w.z));
             pend &= ~(1u << (i * QA + j));
           }
         }
       }
     }
-    if (__all(pend == 0)) break;
-    if (wave_should_bail(A, it)) break;
-    __builtin_amdgcn_s_sleep(1);
-  }
 #pragma unroll
-  for (int i = 0; i < MAXR; ++i) {
-    const int s = wave + 4 * i;
-#pragma unroll
-    for (int j = 0; j < QA; ++j) {
-      const int q = lane + 64 * j;
-      if (s < k && q < nq) {
-        *reinterpret_cast<float2*>(as + apos(s, 2 * q, I)) =
-            make_float2(__uint_as_float(p[i][j].x), __uint_as_float(p[i][j].z));
+    for (int i = 0; i < MAXR; ++i) {
+      const unsigned m = ((1u << QA) - 1u) << (i * QA);
+      if ((todo & (1u << i)) && __all((pend & m) == 0)) {
+        // the chunks came from every lane of this wavefront: its LDS accesses
+        // complete in order, so the reads below see them
+        const int s = wave + 4 * i;
+        accs[i] = down_dot<NJD>(dr[i], as + apos(s, 0, I), I, sw[s], 0.f);
+        todo &= ~(1u << i);
       }
     }
+    if (!todo) break;
+    if (wave_should_bail(A, it)) break;
+    __builtin_amdgcn_s_sleep(1);
   }
 }
 
@@ -822,12 +816,13 @@ __device__ __forceinline__ void role_down(const FusedStepArgs& A, int l, int d, 
     }
   }
   issue_here();
-  wave_wait_routed<QA, (WSX_MAX_K + 3) / 4>(A, tag, as);
+  constexpr int MAXR = (WSX_MAX_K + 3) / 4;   // routed slots per wavefront
+  float accs[MAXR];
+  wave_routed_dots<QA, MAXR>(A, tag, as, dr, R->w[wave].sw, accs);
+  // the shared slot, then the routed slots in slot order: a fixed order
 #pragma unroll
-  for (int i = 0; i < MAXS; ++i) {
-    const int s = wave + 4 * i;
-    if (s < k) acc = down_dot<NJD>(dr[i], as + apos(s, 0, I), I, R->w[wave].sw[s], acc);
-  }
+  for (int i = 0; i < MAXR; ++i)
+    if (wave + 4 * i < k) acc += accs[i];
   acc = sum8(acc);
   if ((lane & 7) == 0) part[wave * kDRows + (lane >> 3)] = acc;
   __syncthreads();
