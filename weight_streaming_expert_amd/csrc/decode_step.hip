@@ -763,12 +763,10 @@ __device__ __forceinline__ void role_down(const FusedStepArgs& A, int l, int d, 
   const int n0 = d * kDRows;
   const unsigned tag = base + l;
   const size_t c2 = (size_t)H * (I / 2), s2 = (size_t)H * (I / 32);
-  constexpr int MAXS = (WSX_MAX_K + 1 + 3) / 4;   // slots per wavefront: s = wave + 4 i
-  DownRegs<NJD> dr[MAXS];
-  // prefetch the shared expert's rows (slot k)
-#pragma unroll
-  for (int i = 0; i < MAXS; ++i)
-    if (wave + 4 * i == k && nslot > k) down_load<NJD>(A.sh2c + (size_t)l * c2, A.sh2s + (size_t)l * s2, I, n0, dr[i]);
+  // the shared expert's slot k belongs to wavefront k % 4: prefetch its rows
+  const bool shared_here = nslot > k && wave == (k & 3);
+  DownRegs<NJD> dsh;
+  if (shared_here) down_load<NJD>(A.sh2c + (size_t)l * c2, A.sh2s + (size_t)l * s2, I, n0, dsh);
   issue_here();
   if (l > 0 && threadIdx.x == 0) sleep_on_tag(A, hx_buf(A, l, my_copy(kCopiesH)), H / 2 - 1, base + l - 1);
   __syncthreads();
@@ -793,13 +791,9 @@ __device__ __forceinline__ void role_down(const FusedStepArgs& A, int l, int d, 
   // the shared expert first (owned by wavefront k % 4): its activations are
   // stored before the routing is known, so this wait overlaps the routing's
   float acc = 0.f;
-#pragma unroll
-  for (int i = 0; i < MAXS; ++i) {
-    const int s = wave + 4 * i;
-    if (s == k && s < nslot) {
-      wave_wait_slot<QA>(A, s, tag, as + apos(s, 0, I));
-      acc = down_dot<NJD>(dr[i], as + apos(s, 0, I), I, 1.0f, acc);
-    }
+  if (shared_here) {
+    wave_wait_slot<QA>(A, k, tag, as + apos(k, 0, I));
+    acc = down_dot<NJD>(dsh, as + apos(k, 0, I), I, 1.0f, acc);
   }
   route_topk(A, tag, R);
   route_weights(A, R);
@@ -807,8 +801,10 @@ __device__ __forceinline__ void role_down(const FusedStepArgs& A, int l, int d, 
     if (A.ids_trace) A.ids_trace[(size_t)l * k + threadIdx.x] = R->w[0].rid[threadIdx.x];
     if (A.w_trace) A.w_trace[(size_t)l * k + threadIdx.x] = R->w[0].rw[threadIdx.x];
   }
+  constexpr int MAXR = (WSX_MAX_K + 3) / 4;   // routed slots per wavefront: s = wave + 4 i
+  DownRegs<NJD> dr[MAXR];
 #pragma unroll
-  for (int i = 0; i < MAXS; ++i) {
+  for (int i = 0; i < MAXR; ++i) {
     const int s = wave + 4 * i;
     if (s < k) {
       const int e = min(max(R->w[wave].sid[s], 0), E - 1);
@@ -816,7 +812,6 @@ __device__ __forceinline__ void role_down(const FusedStepArgs& A, int l, int d, 
     }
   }
   issue_here();
-  constexpr int MAXR = (WSX_MAX_K + 3) / 4;   // routed slots per wavefront
   float accs[MAXR];
   wave_routed_dots<QA, MAXR>(A, tag, as, dr, R->w[wave].sw, accs);
   // the shared slot, then the routed slots in slot order: a fixed order
