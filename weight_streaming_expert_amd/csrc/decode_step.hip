@@ -16,7 +16,7 @@
 //
 //   per layer l:  R (router rows)  S (shared gate/up tiles)  G (routed gate/up
 //                 tiles, k slots)  D (down rows over all slots, + residual)
-//   then:         head rows and a two-level argmax
+//   then:         head rows and one argmax over all of them (a 64-bit atomic max)
 //
 // A workgroup only ever waits for data produced by workgroups with a LOWER
 // index.  Workgroups are dispatched in index order, so the lowest-indexed
@@ -50,7 +50,6 @@ constexpr int kRouteCand = 8;      // groups whose logits are ranked in full (>=
 static_assert(kRouteCand >= WSX_MAX_K && kRouteCand * 8 == kRouteGroups, "routing candidate layout");
 constexpr int kGRows = 16;         // intermediate values per S/G workgroup
 constexpr int kDRows = 8;          // output rows per D workgroup
-constexpr int kHeadGroup = 32;     // head workgroups per first-level argmax group
 constexpr int kSpinMax = 1 << 17;  // polls before a wait gives up
 constexpr unsigned kEpochMod = (1u << 24) - 1;   // epochs cycle in [0, kEpochMod)
 // Copies of each exchange buffer: every consumer polls the copy picked by its
@@ -58,7 +57,6 @@ constexpr unsigned kEpochMod = (1u << 24) - 1;   // epochs cycle in [0, kEpochMo
 constexpr int kCopiesH = 8;        // residual stream
 constexpr int kCopiesLg = 16;      // router logits
 constexpr int kCopiesA = 8;        // expert activations
-constexpr unsigned kHeadTag = 255;               // layer field of the head's tags
 
 struct Ctl {   // control words, each on its own 256-byte line
   unsigned epoch;
@@ -67,18 +65,17 @@ struct Ctl {   // control words, each on its own 256-byte line
   unsigned pad1[63];
   unsigned top_counter;
   unsigned pad2[63];
+  unsigned long long best;   // the step's best head rank key so far (0: none)
+  unsigned pad3[62];
 };
 
 }  // namespace
 
 struct FusedBufs {
   void* ctl;                 // Ctl
-  unsigned* group_counter;   // [n_groups], 64-byte stride
   uint2* hx;                 // [kCopiesH][2][H/2] (bf16 pair, tag); h_l lives in [.][l & 1] (l >= 1)
   uint2* lg;                 // [kCopiesLg][E] (logit, tag) of the current layer
   uint2* a;                  // [kCopiesA][nslot][I] (activation, tag) of the current layer
-  uint4* hpart;              // [n_head] (value, index, tag, -)
-  uint4* gpart;              // [n_groups]
 };
 
 struct FusedStepArgs {
@@ -97,7 +94,7 @@ struct FusedStepArgs {
   float* w_trace;
   FusedBufs b;
   int L, H, I, E, k, V;
-  int nslot, nR, nS, nG, nD, per_layer, n_head, n_groups;
+  int nslot, nR, nS, nG, nD, per_layer, n_head;
   int block0;   // index of this launch's first workgroup in the step's workgroup order
 };
 
@@ -862,7 +859,6 @@ __device__ __forceinline__ void role_head(const FusedStepArgs& A, int hb, unsign
   const int H = A.H, V = A.V, L = A.L;
   const int NG = (V + 3) / 4;
   const int stride = A.n_head * 4;
-  const unsigned htag = base + kHeadTag;
   int grp = hb * 4 + wave;
   uint4 w[HJ];
   float sc = 0.f;
@@ -904,47 +900,25 @@ __device__ __forceinline__ void role_head(const FusedStepArgs& A, int hb, unsign
   wave_argmax(bv, bi);
   if (lane == 0) { wv_[wave] = bv; wi_[wave] = bi; }
   __syncthreads();
+  // the workgroup's best (value, row) joins the step's maximum rank key: one
+  // 64-bit atomic max orders by value, then lower row, as `better` does
   if (threadIdx.x == 0) {
     float v = wv_[0];
     int i = wi_[0];
     for (int q = 1; q < 4; ++q)
       if (better(wv_[q], wi_[q], v, i)) { v = wv_[q]; i = wi_[q]; }
-    st_coh16(A.b.hpart, (uint32_t)hb * 16, make_uint4(__float_as_uint(v), (uint32_t)i, htag, 0));
+    const RankKey key = (v == v) ? rank_key(v, i) : 0ull;   // a NaN never wins
+    __hip_atomic_fetch_max(&ctl(A)->best, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  // first level: the last workgroup of each group of kHeadGroup reduces the group
-  const int gid = hb / kHeadGroup;
-  const int g0 = gid * kHeadGroup;
-  const int gn = min(kHeadGroup, A.n_head - g0);
-  if (!last_block_arrived(A.b.group_counter + gid * 16, gn, flag)) return;
-  if (threadIdx.x < 64) {
-    float v = -INFINITY;
-    int i = 0x7FFFFFFF;
-    if (lane < gn) {
-      const uint4 p = ld_coh16(A.b.hpart, (uint32_t)(g0 + lane) * 16);
-      if (p.z != htag) raise_err(A);
-      v = __uint_as_float(p.x);
-      i = (int)p.y;
-    }
-    wave_argmax(v, i);
-    if (lane == 0) st_coh16(A.b.gpart, (uint32_t)gid * 16, make_uint4(__float_as_uint(v), (uint32_t)i, htag, 0));
-  }
-  // second level: the last group reduces the groups, publishes the argmax and
-  // advances the epoch for the next step
-  if (!last_block_arrived(&ctl(A)->top_counter, A.n_groups, flag)) return;
-  if (threadIdx.x < 64) {
-    float v = -INFINITY;
-    int i = 0x7FFFFFFF;
-    for (int q = lane; q < A.n_groups; q += 64) {
-      const uint4 p = ld_coh16(A.b.gpart, (uint32_t)q * 16);
-      if (p.z != htag) raise_err(A);
-      if (better(__uint_as_float(p.x), (int)p.y, v, i)) { v = __uint_as_float(p.x); i = (int)p.y; }
-    }
-    wave_argmax(v, i);
-    if (lane == 0) {
-      A.argmax[0] = err_set(A) ? -1 : i;
-      const unsigned ep = (unsigned)ld_dev(reinterpret_cast<const int*>(&ctl(A)->epoch));
-      st_dev(reinterpret_cast<int*>(&ctl(A)->epoch), (int)((ep + 1) % kEpochMod));
-    }
+  // the last workgroup to arrive reads the maximum, publishes the argmax,
+  // clears the maximum and advances the epoch for the next step
+  if (!last_block_arrived(&ctl(A)->top_counter, A.n_head, flag)) return;
+  if (threadIdx.x == 0) {
+    const RankKey best = __hip_atomic_load(&ctl(A)->best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&ctl(A)->best, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    A.argmax[0] = (err_set(A) || best == 0ull) ? -1 : key_id(best);
+    const unsigned ep = (unsigned)ld_dev(reinterpret_cast<const int*>(&ctl(A)->epoch));
+    st_dev(reinterpret_cast<int*>(&ctl(A)->epoch), (int)((ep + 1) % kEpochMod));
   }
 }
 
@@ -959,7 +933,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) de
   __shared__ float wv_[4];
   __shared__ int wi_[4];
   __shared__ int flag;
-  // tags: (epoch + 1) in the upper 24 bits, the layer (or 255 for the head) below
+  // tags: (epoch + 1) in the upper 24 bits, the layer below
   const unsigned base = ((unsigned)ld_dev(reinterpret_cast<const int*>(&ctl(A)->epoch)) + 1u) << 8;
   const int bid = A.block0 + (int)blockIdx.x;
   if (bid >= A.L * A.per_layer) {
@@ -1011,8 +985,8 @@ bool is_tiny(const Shape& s) {
 inline size_t al(size_t n) { return (n + 255) & ~(size_t)255; }
 
 struct FusedLayout {
-  size_t ctl, gcnt, hx, lg, a, hpart, gpart, total;
-  int n_head, n_groups;
+  size_t ctl, hx, lg, a, total;
+  int n_head;
 };
 
 int fused_head_blocks(int V) {
@@ -1025,15 +999,11 @@ FusedLayout fused_layout(int H, int I, int E, int k, int V) {
   FusedLayout f;
   const int nslot = k + 1;
   f.n_head = fused_head_blocks(V);
-  f.n_groups = (f.n_head + kHeadGroup - 1) / kHeadGroup;
   f.ctl = 0;
-  f.gcnt = al(f.ctl + sizeof(Ctl));
-  f.hx = al(f.gcnt + (size_t)f.n_groups * 64);
+  f.hx = al(f.ctl + sizeof(Ctl));
   f.lg = al(f.hx + (size_t)kCopiesH * 2 * (H / 2) * 8);
   f.a = al(f.lg + (size_t)kCopiesLg * E * 8);
-  f.hpart = al(f.a + (size_t)kCopiesA * nslot * I * 8);
-  f.gpart = al(f.hpart + (size_t)f.n_head * 16);
-  f.total = al(f.gpart + (size_t)f.n_groups * 16);
+  f.total = al(f.a + (size_t)kCopiesA * nslot * I * 8);
   return f;
 }
 
@@ -1072,12 +1042,9 @@ hipError_t launch_fused_step(const wsx_moe_stack* sk, const uint16_t* h_in, cons
   A.hq = hq; A.hs = hs; A.h_in = h_in; A.h_out = h_out; A.logits = logits; A.argmax = argmax;
   A.h_trace = h_trace; A.u_trace = u_trace; A.ids_trace = ids_trace; A.w_trace = w_trace;
   A.b.ctl = base + f.ctl;
-  A.b.group_counter = reinterpret_cast<unsigned*>(base + f.gcnt);
   A.b.hx = reinterpret_cast<uint2*>(base + f.hx);
   A.b.lg = reinterpret_cast<uint2*>(base + f.lg);
   A.b.a = reinterpret_cast<uint2*>(base + f.a);
-  A.b.hpart = reinterpret_cast<uint4*>(base + f.hpart);
-  A.b.gpart = reinterpret_cast<uint4*>(base + f.gpart);
   A.L = L; A.H = H; A.I = I; A.E = E; A.k = k; A.V = V;
   A.nslot = k + 1;
   A.nR = E / kRRows;
@@ -1086,7 +1053,6 @@ hipError_t launch_fused_step(const wsx_moe_stack* sk, const uint16_t* h_in, cons
   A.nD = H / kDRows;
   A.per_layer = A.nR + A.nS + A.nG + A.nD;
   A.n_head = f.n_head;
-  A.n_groups = f.n_groups;
   const size_t lds = fused_lds_bytes(H, I, k);
   const int total = L * A.per_layer + A.n_head;
   const int rb = sk->router_dtype == WSX_DTYPE_F32 ? 4 : 2;
