@@ -286,10 +286,12 @@ def _timed_graph(torch, fn, flush=None, reps=100):
 def breakdown(torch, ops, configs, inputs, dev, stack, head, head_w, lw0, wl, quant_us):
     m = wl.moe
     H, I, E, k, V = m.H, m.I, m.E, m.k, head.V
-    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush_buf = torch.ones(1 << 27, dtype=torch.int64, device=dev)   # 1 GiB
 
     def flush():
-        flush_buf.add_(1)
+        # a read-only sweep: it evicts the caches without leaving dirty lines
+        # whose write-back would land inside the next timed kernel
+        flush_buf.sum()
 
     out = {}
     layer = dict(router=stack.w_router[0], w13c=stack.w13_codes[0], w13s=stack.w13_scales[0],
