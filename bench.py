@@ -192,7 +192,7 @@ def main():
     head_us = e0.elapsed_time(e1) * 1e3 / (10 * reps)
     head_bytes = configs.head_bytes(V, H, 1, True)
     head_gbps = head_bytes / (head_us * 1e-6) / 1e9
-    head_kernel = {"kernel": "lm_head_kernel<fp8,T=1> (FP8 LM-head GEMV + argmax, standalone)", "bound": "hbm",
+    head_kernel = {"kernel": "lm_head_wide_kernel<fp8> (FP8 LM-head GEMV + argmax, 1 token, standalone)", "bound": "hbm",
                    "achieved": round(head_gbps, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                    "frac": round(head_gbps / PEAK_GBPS, 4), "bytes_per_launch": head_bytes,
                    "us_per_launch": round(head_us, 2)}

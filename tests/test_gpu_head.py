@@ -103,9 +103,10 @@ def test_heads_ragged_shapes(ops, V, K, T):
     assert np.array_equal(P.np_(am2), P.np_(ops.lm_head_gemv_fp8_argmax(q, s, xd)[1]))
 
 
-def test_fp8_head_exact_small_integers(ops):
+@pytest.mark.parametrize("T", [1, 4])
+def test_fp8_head_exact_small_integers(ops, T):
     g = np.random.default_rng(3)
-    V, K, T = 3001, 2560, 4
+    V, K = 3001, 2560
     q = g.integers(0, 256, size=(V, K)).astype(np.uint8)
     big = ((q >> 3) & 0xF) > 7
     q[big] = (q[big] & 0x87) | 0x38          # |value| < 2: every partial sum is an exact binary32
@@ -119,19 +120,22 @@ def test_fp8_head_exact_small_integers(ops):
     assert np.array_equal(P.np_(am), np.argmax(exact, axis=1))
 
 
-def test_head_ties_go_to_lowest_index(ops):
+@pytest.mark.parametrize("T", [1, 2])
+def test_head_ties_go_to_lowest_index(ops, T):
+    """Rows 777, 5001 and 19000 tie for the top logit; they are read by
+    different workgroups, and the argmax takes the lowest row."""
     V, K = 20000, 2560
     w = inputs.normal_bf16((12,), (V, K), 0.02)
     w[[777, 5001, 19000]] = 0x3D4D                        # bf16 0.05 in every element
-    x = np.full((2, K), 0x3F80, dtype=np.uint16)          # all ones: rows 777, 5001, 19000 tie for the top
+    x = np.full((T, K), 0x3F80, dtype=np.uint16)          # all ones: rows 777, 5001, 19000 tie for the top
     wd = P.to_dev_bf16(w)
     q, s = ops.lm_head_quantize_fp8(wd)
     logits, am = ops.lm_head_gemv_fp8_argmax(q, s, P.to_dev_bf16(x))
     lg = P.np_(logits)
     assert lg[0, 777] == lg[0, 5001] == lg[0, 19000] == lg[0].max()
-    assert list(P.np_(am)) == [777, 777]
+    assert list(P.np_(am)) == [777] * T
     _, amb = ops.lm_head_gemv_bf16_argmax(wd, P.to_dev_bf16(x))
-    assert list(P.np_(amb)) == [777, 777]
+    assert list(P.np_(amb)) == [777] * T
 
 
 def test_head_is_deterministic(ops, full_head):

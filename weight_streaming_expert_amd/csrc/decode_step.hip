@@ -292,20 +292,6 @@ __device__ __forceinline__ uint4 ld16_stream(const void* p) {
 
 // ---------------------------------------------------------------- routing
 
-// A logit's rank key: the value's bits mapped to an unsigned integer that
-// orders as the value does (-0 taken as +0), above the complement of the id.
-// A larger key ranks before: larger value, then lower id.
-using RankKey = unsigned long long;
-__device__ __forceinline__ RankKey rank_key(float v, int id) {
-  const unsigned b = __float_as_uint(v + 0.0f);
-  const unsigned o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return ((RankKey)o << 32) | (unsigned)~id;
-}
-__device__ __forceinline__ float key_value(RankKey key) {
-  const unsigned o = (unsigned)(key >> 32);
-  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
-}
-__device__ __forceinline__ int key_id(RankKey key) { return (int)~(unsigned)key; }
 
 template <int CTRL>
 __device__ __forceinline__ int dpp_i(int v) { return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false); }

@@ -236,6 +236,124 @@ __global__ void __launch_bounds__(256) lm_head_kernel(const uint8_t* __restrict_
   }
 }
 
+
+// ---------------------------------------------------------------- LM head, one token, wide workgroups
+
+// The 1-token head ([saipien] "Stop hauling the vocabulary in full
+// precision": the whole head is read for every token) as one 1024-thread
+// workgroup per CU.  Wavefront v of workgroup b takes row groups
+// b * 16 + v + P * 16 * i, so a CU's 16 wavefronts stream neighbouring rows;
+// each keeps the next group's loads in flight while it reduces the current
+// one, and issues its first group's loads before the activations are staged.
+// RL lanes per row (RPW = 64 / RL rows per wavefront group), GPL granules per
+// lane.  The activations sit in LDS with granule g at byte g * GS (a stride
+// that lets the RL lanes of a row read their granules without bank
+// conflicts).  The argmax is one 64-bit atomic maximum of rank keys (value,
+// then lower row), read by the last workgroup to finish, which resets it.
+template <int WT, int GPL, int RL>
+struct HeadGroup {
+  uint4 w[GPL];
+  float sc;
+};
+
+template <int WT, int GPL, int RL>
+__device__ __forceinline__ void head_group_load(__amdgpu_buffer_rsrc_t W, const float* row_scale, int V, int G,
+                                                uint32_t row_bytes, int grp, HeadGroup<WT, GPL, RL>& g) {
+  constexpr int RPW = 64 / RL;
+  const int lane = threadIdx.x & 63;
+  const int row = grp * RPW + lane / RL, c = lane % RL;
+  const bool ok = row < V;
+  const uint32_t o = (uint32_t)(ok ? row : 0) * row_bytes + (uint32_t)c * 16;
+#pragma unroll
+  for (int j = 0; j < GPL; ++j)
+    g.w[j] = (ok && c + RL * j < G)
+                 ? __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(W, o + 16 * RL * j, 0, 2))
+                 : make_uint4(0, 0, 0, 0);
+  g.sc = 1.0f;
+  if (WT == W_FP8 && ok && c == 0) g.sc = row_scale[row];
+}
+
+template <int WT, int GPL, int RL>
+__global__ void __launch_bounds__(1024) lm_head_wide_kernel(const uint8_t* __restrict__ W,
+                                                            const float* __restrict__ row_scale, int V, int K,
+                                                            const uint16_t* __restrict__ x, float* __restrict__ logits,
+                                                            int32_t* __restrict__ argmax, unsigned* counter,
+                                                            unsigned long long* best) {
+  constexpr int EPG = WTraits<WT>::EPG, DW = EPG / 2, RPW = 64 / RL, NW = 16;
+  constexpr int GS = (WT == W_FP8) ? 48 : 16;   // LDS bytes per activation granule
+  extern __shared__ __attribute__((aligned(16))) uint8_t xsb[];
+  __shared__ float wv_[NW];
+  __shared__ int wi_[NW];
+  __shared__ int flag;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, c = lane % RL;
+  const int G = K / EPG;
+  const uint32_t row_bytes = (uint32_t)K * WTraits<WT>::ESZ;
+  const __amdgpu_buffer_rsrc_t Wr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(W), 0, 0x7FFFFFFF, 0x00020000);
+  const int NG = (V + RPW - 1) / RPW;
+  const int stride = (int)gridDim.x * NW;
+  int grp = (int)blockIdx.x * NW + wave;
+  // x first (one 16-byte chunk of 8 bf16 per thread, K <= 8192), then the
+  // first group: loads complete in issue order, so the staging below waits
+  // for x alone and the group stays in flight across the barrier
+  uint4 xv = make_uint4(0, 0, 0, 0);
+  if (t < K / 8) xv = ld16(x + 8 * t);
+  HeadGroup<WT, GPL, RL> cur;
+  if (grp < NG) head_group_load<WT, GPL, RL>(Wr, row_scale, V, G, row_bytes, grp, cur);
+  issue_here();
+  if (t < K / 8) *reinterpret_cast<uint4*>(xsb + (8 * t / EPG) * GS + (8 * t % EPG) * 2) = xv;
+  lds_barrier();
+  float bv = -INFINITY;
+  int bi = 0x7FFFFFFF;
+  while (grp < NG) {
+    HeadGroup<WT, GPL, RL> nxt;
+    const int ng = grp + stride;
+    if (ng < NG) head_group_load<WT, GPL, RL>(Wr, row_scale, V, G, row_bytes, ng, nxt);
+    issue_here();
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < GPL; ++j) {
+      const int g = c + RL * j;
+      if (g < G) {
+        uint32_t xp[DW];
+        const uint4* src = reinterpret_cast<const uint4*>(xsb + g * GS);
+#pragma unroll
+        for (int d = 0; d < DW / 4; ++d) {
+          const uint4 v = src[d];
+          xp[4 * d] = v.x; xp[4 * d + 1] = v.y; xp[4 * d + 2] = v.z; xp[4 * d + 3] = v.w;
+        }
+        acc += granule_dot<WT>(cur.w[j], xp);
+      }
+    }
+    acc = sum16(acc);
+    if constexpr (RL == 32) acc += __shfl_xor(acc, 16);
+    const int row = grp * RPW + lane / RL;
+    if (c == 0 && row < V) {
+      const float l = (WT == W_FP8) ? acc * cur.sc : acc;
+      if (logits) logits[row] = l;
+      if (better(l, row, bv, bi)) { bv = l; bi = row; }
+    }
+    cur = nxt;
+    grp = ng;
+  }
+  wave_argmax(bv, bi);
+  if (lane == 0) { wv_[wave] = bv; wi_[wave] = bi; }
+  lds_barrier();
+  if (t == 0) {
+    float v = wv_[0];
+    int i = wi_[0];
+    for (int q = 1; q < NW; ++q)
+      if (better(wv_[q], wi_[q], v, i)) { v = wv_[q]; i = wi_[q]; }
+    const RankKey key = (v == v) ? rank_key(v, i) : 0ull;   // a NaN never wins
+    __hip_atomic_fetch_max(best, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (!last_block_arrived(counter, gridDim.x, &flag)) return;
+  if (t == 0) {
+    const RankKey b = __hip_atomic_load(best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(best, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    argmax[0] = b == 0ull ? -1 : key_id(b);
+  }
+}
+
 // ---------------------------------------------------------------- router + top-k
 
 // Top-k of one token's E logits (E <= 4 * 256) by the whole 256-thread
@@ -479,9 +597,43 @@ int head_grid(int V) {
   return g < 1 ? 1 : (g > kHeadMaxGrid ? kHeadMaxGrid : g);
 }
 
+// The wide 1-token head for the shapes it is compiled for: one workgroup per
+// CU; weights addressed with 32-bit offsets, so the head must be below 2 GiB.
+static hipError_t launch_head_wide(int wt, const void* W, const float* s, int V, int K, const uint16_t* x,
+                                   float* logits, int32_t* argmax, unsigned* counter, unsigned long long* best,
+                                   hipStream_t st, bool* done) {
+  *done = false;
+  if ((size_t)V * K * (wt == W_FP8 ? 1 : 2) >= ((size_t)1 << 31)) return hipSuccess;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    return hipSuccess;
+  const int epg = wt == W_FP8 ? 16 : 8, gs = wt == W_FP8 ? 48 : 16;
+  const size_t lds = (size_t)(K / epg) * gs;
+#define WSX_WIDE(WTV, GPLV, RLV)                                                                                   \
+  {                                                                                                              \
+    lm_head_wide_kernel<WTV, GPLV, RLV><<<cus, 1024, lds, st>>>((const uint8_t*)W, s, V, K, x, logits, argmax,   \
+                                                                 counter, best);                                 \
+    *done = true;                                                                                                \
+    return hipGetLastError();                                                                                    \
+  }
+  if (wt == W_FP8 && K == 2560) WSX_WIDE(W_FP8, 10, 16)
+  if (wt == W_FP8 && K == 256) WSX_WIDE(W_FP8, 1, 16)
+  if (wt == W_BF16 && K == 2560) WSX_WIDE(W_BF16, 10, 32)
+  if (wt == W_BF16 && K == 256) WSX_WIDE(W_BF16, 1, 32)
+#undef WSX_WIDE
+  return hipSuccess;
+}
+
 hipError_t launch_lm_head(int wt, const void* W, const float* s, int V, int K, const uint16_t* x, int T, int norm,
                           uint16_t* u_out, float* logits, int32_t* argmax, void* ws, hipStream_t st) {
   unsigned* counter = reinterpret_cast<unsigned*>(ws);
+  if (T == 1 && !norm) {
+    bool done = false;
+    const hipError_t e = launch_head_wide(wt, W, s, V, K, x, logits, argmax, counter,
+                                          reinterpret_cast<unsigned long long*>((char*)ws + 64), st, &done);
+    if (done || e != hipSuccess) return e;
+  }
   const int grid = head_grid(V);
   float* pv = reinterpret_cast<float*>((char*)ws + 256);
   int* pi = reinterpret_cast<int*>((char*)ws + 256 + (size_t)kHeadMaxGrid * WSX_MAX_T * 4);

@@ -181,6 +181,22 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
+// A value's rank key: the value's bits mapped to an unsigned integer that
+// orders as the value does (-0 taken as +0), above the complement of the id.
+// A larger key ranks before: larger value, then lower id.
+using RankKey = unsigned long long;
+__device__ __forceinline__ RankKey rank_key(float v, int id) {
+  const unsigned b = __float_as_uint(v + 0.0f);
+  const unsigned o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((RankKey)o << 32) | (unsigned)~id;
+}
+__device__ __forceinline__ float key_value(RankKey key) {
+  const unsigned o = (unsigned)(key >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+__device__ __forceinline__ int key_id(RankKey key) { return (int)~(unsigned)key; }
+
+
 // ---------------------------------------------------------------- memory
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -213,6 +229,12 @@ __device__ __forceinline__ void stage_to_lds(const void* __restrict__ src, void*
 // particular until its device-coherent stores have been acknowledged.  The
 // memory clobber keeps the compiler from moving memory accesses across it.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Workgroup barrier for data exchanged through LDS only.  __syncthreads() is
+// also a workgroup-scope release fence, which waits for every outstanding
+// vector memory access of the wavefront (vmcnt(0)), including loads meant to
+// stay in flight across the barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Compiler-only barrier: keeps the loads issued before it (prefetches meant to
 // be in flight during a wait) from being sunk past it to their first use.
