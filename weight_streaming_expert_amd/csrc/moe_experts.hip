@@ -399,11 +399,23 @@ __global__ void __launch_bounds__(256) moe_down_grouped_kernel(
         sc[b][r] = kb < NB ? e8m0_to_f32(S[row * rows + kb]) : 0.f;
       }
     }
-    // this slot's activations -> LDS
+    // this slot's activations -> LDS, every load issued before the first
+    // store (T*I/4 chunks over the 64 lanes; I <= 256 * NKB)
     const float4* src = reinterpret_cast<const float4*>(a_in + (size_t)s * T * I);
-    for (int q = lane; q < T * I / 4; q += 64) {
-      const int t = (4 * q) / I, i = (4 * q) % I;
-      *reinterpret_cast<float4*>(aw + t * lstride + dpos(i)) = src[q];
+    const int nq = T * I / 4;
+    float4 av4[T * NKB];
+#pragma unroll
+    for (int j = 0; j < T * NKB; ++j) {
+      const int q = lane + 64 * j;
+      av4[j] = q < nq ? src[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int j = 0; j < T * NKB; ++j) {
+      const int q = lane + 64 * j;
+      if (q < nq) {
+        const int t = (4 * q) / I, i = (4 * q) % I;
+        *reinterpret_cast<float4*>(aw + t * lstride + dpos(i)) = av4[j];
+      }
     }
 #pragma unroll
     for (int b = 0; b < NKB; ++b) {
