@@ -88,7 +88,7 @@ def test_bf16_head_full_size(ops, full_head, T):
     P.check_head(None, None, x, P.np_(logits), P.np_(am), bf16_w=full_head["w"])
 
 
-@pytest.mark.parametrize("V,K", [(1, 32), (5, 96), (4099, 256), (1000, 2560), (300, 4096)])
+@pytest.mark.parametrize("V,K", [(1, 32), (5, 96), (17, 256), (4099, 256), (3, 2560), (1000, 2560), (300, 4096)])
 @pytest.mark.parametrize("T", [1, 2, 3, 4])
 def test_heads_ragged_shapes(ops, V, K, T):
     w = inputs.normal_bf16((9, V, K), (V, K), 0.02)
