@@ -357,8 +357,9 @@ __global__ void __launch_bounds__(1024) lm_head_wide_kernel(const uint8_t* __res
 
 // ---------------------------------------------------------------- LM head, 2-4 tokens, on the matrix cores
 
-// The verify pass's head ([saipien] "Draft three tokens, verify four": one
-// read of the head for up to four positions) as a small dense contraction on
+// The verify pass's head ([saipien] "Draft three tokens, verify four": the
+// verify pass scores four positions; here one read of the head serves all
+// of them) as a small dense contraction on
 // v_mfma_f32_16x16x32_bf16: 16 head rows x 32 K values x 16 token columns
 // (columns past T are zero).  E4M3 codes are decoded to bf16 exactly; the row
 // scale multiplies the fp32 sum.  One 1024-thread workgroup per CU; the work
