@@ -321,6 +321,22 @@ def breakdown(torch, ops, configs, inputs, dev, stack, head, head_w, lw0, wl, qu
         b = configs.head_bytes(V, H, T, True)
         t.update(bytes=b, GBps=round(b / (t["median_us"] * 1e-6) / 1e9, 1))
         out[f"lm_head_fp8_t{T}"] = t
+    # the sampling epilogue at the GSM8K settings (temperature 0.6, top-k 29,
+    # top-p 0.95): the sampler alone on resident logits, and head + sampler
+    for T in (1, 4):
+        xt = x[:T].contiguous()
+        u = torch.from_numpy(inputs.uniform_f32((wl.seed, 9, T), (T,))).to(dev)
+        logits_t, _ = head.gemv_argmax(xt)
+        sws = ops.workspace(ops._lib.load().wsx_sample_workspace_bytes(T, V, 29), dev)
+        t = _timed_graph(torch, lambda: ops.lm_sample_topk_topp(logits_t, 0.6, 29, 0.95, u, ws=sws), flush)
+        t.update(bytes=T * V * 4)
+        out[f"sample_topk_topp_t{T}"] = t
+        fws = ops.workspace(ops._lib.load().wsx_lm_head_sample_workspace_bytes(T, V, H, 29), dev)
+        t = _timed_graph(torch, lambda: ops.lm_head_gemv_fp8_sample(head.q, head.s, xt, 0.6, 29, 0.95, u, ws=fws),
+                         flush)
+        b = configs.head_bytes(V, H, T, True)
+        t.update(bytes=b, GBps=round(b / (t["median_us"] * 1e-6) / 1e9, 1))
+        out[f"lm_head_fp8_sample_t{T}"] = t
     hws = ops.workspace(ops.lm_head_workspace_bytes(1, V, H), dev)
     x1 = x[:1].contiguous()
     t = _timed_graph(torch, lambda: ops.lm_head_gemv_bf16_argmax(head_w, x1, ws=hws), flush)

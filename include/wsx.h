@@ -173,6 +173,47 @@ wsx_status lm_head_gemv_bf16_argmax(const uint16_t* w, int V, int K, const uint1
                                     void* stream);
 
 /*
+ * lm_sample_topk_topp — one sampled token per row of the head's logits, with
+ * temperature, top-k and top-p, the uniform draw supplied by the caller.
+ *
+ * [ncij] "What happens on a real workload?": the GSM8K run samples with
+ * temperature 0.6, top_p 0.95 and top_k 29.  The pages give only the three
+ * settings; the steps are (binary32, in this order):
+ *   z_0 >= ... >= z_{k-1}: the top_k logits, ties to the LOWER id;
+ *   e_i = exp((z_i - z_0) / temperature);  c_i = e_0 + ... + e_i;
+ *   m = the first i with c_i >= top_p * c_{k-1}   (ranks 0..m are kept);
+ *   token = id of the first rank j <= m with c_j > u * c_m (rank m if none).
+ *
+ * logits float [T][V]; uniforms float [T], each in [0, 1); token int32 [T];
+ * topk_ids int32 [T][top_k] (ranked ids) and topk_probs float [T][top_k]
+ * (e_i / c_m for i <= m, else 0) may be NULL.
+ * Limits: 1 <= T <= 4, 1 <= top_k <= min(64, V), V <= 524,224,
+ * temperature > 0 and finite, 0 < top_p <= 1 (else WSX_ERR_SHAPE or
+ * WSX_ERR_UNSUPPORTED).  Workspace: wsx_sample_workspace_bytes(T, V, top_k)
+ * (no zero fill needed).
+ */
+size_t wsx_sample_workspace_bytes(int T, int V, int top_k);
+wsx_status lm_sample_topk_topp(const float* logits, int V, int T, float temperature, int top_k,
+                               float top_p, const float* uniforms, int32_t* token,
+                               int32_t* topk_ids, float* topk_probs, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/*
+ * lm_head_gemv_fp8_sample — the FP8 head of lm_head_gemv_fp8_argmax followed
+ * on the same stream by lm_sample_topk_topp on its logits: the sampling
+ * decode of [ncij] "What happens on a real workload?" in place of greedy.
+ * logits float [T][V] is required (the sampler reads it).  Limits: those of
+ * both calls.  Workspace: wsx_lm_head_sample_workspace_bytes(T, V, K, top_k),
+ * zero-filled before its first use.
+ */
+size_t wsx_lm_head_sample_workspace_bytes(int T, int V, int K, int top_k);
+wsx_status lm_head_gemv_fp8_sample(const uint8_t* q, const float* row_scale, int V, int K,
+                                   const uint16_t* x, int T, float temperature, int top_k,
+                                   float top_p, const float* uniforms, float* logits,
+                                   int32_t* token, int32_t* topk_ids, float* topk_probs,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Weights of L stacked MoE layers of one shape, each tensor one contiguous
  * allocation with a leading [L] axis:
  *   w_router  [L][E][H] (bf16 or fp32, router_dtype)

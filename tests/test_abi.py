@@ -122,3 +122,30 @@ def test_decode_step_argument_errors():
     assert f(*args(st=bad)) == 2
     need = lib.wsx_decode_step_workspace_bytes(1, 2560, 768, 512, 8, 157184)
     assert need > lib.wsx_moe_workspace_bytes(1, 2560, 768, 512, 8)
+
+
+def sample(lo=FAKE, V=157184, T=1, temp=0.6, k=29, p=0.95, u=FAKE, tok=FAKE, ws=FAKE, wsb=1 << 24):
+    return _lib.load().lm_sample_topk_topp(lo, V, T, temp, k, p, u, tok, None, None, ws, wsb, None)
+
+
+def test_sample_argument_errors():
+    lib = _lib.load()
+    assert sample(lo=None) == 1 and sample(u=None) == 1 and sample(tok=None) == 1
+    assert sample(T=0) == 2 and sample(T=5) == 4
+    assert sample(k=0) == 2 and sample(k=65) == 4 and sample(V=10, k=11) == 2
+    assert sample(temp=0.0) == 2 and sample(temp=-1.0) == 2 and sample(temp=float("inf")) == 2
+    assert sample(temp=float("nan")) == 2
+    assert sample(p=0.0) == 2 and sample(p=1.5) == 2 and sample(p=float("nan")) == 2
+    assert sample(V=8191 * 64 + 1) == 4 and sample(V=8191 * 64, k=64, wsb=0) == 5   # largest V passes the shape checks
+    assert sample(ws=None) == 5 and sample(ws=MIS) == 3
+    need = lib.wsx_sample_workspace_bytes(1, 157184, 29)
+    assert need == 2456 * 29 * 8            # 64-logit chunks
+    assert sample(wsb=need - 1) == 5
+    assert lib.wsx_sample_workspace_bytes(1, 10, 11) == 0
+    head_need = lib.wsx_lm_head_sample_workspace_bytes(4, 157184, 2560, 29)
+    assert head_need == lib.wsx_lm_head_workspace_bytes(4, 157184, 2560) + 256 + 4 * 2456 * 29 * 8
+    f = lib.lm_head_gemv_fp8_sample
+    assert f(None, FAKE, 157184, 2560, FAKE, 1, 0.6, 29, 0.95, FAKE, FAKE, FAKE, None, None, FAKE, head_need, None) == 1
+    assert f(FAKE, FAKE, 157184, 2560, FAKE, 1, 0.6, 29, 0.95, FAKE, None, FAKE, None, None, FAKE, head_need, None) == 1
+    assert f(FAKE, FAKE, 157184, 100, FAKE, 1, 0.6, 29, 0.95, FAKE, FAKE, FAKE, None, None, FAKE, head_need, None) == 2
+    assert f(FAKE, FAKE, 157184, 2560, FAKE, 1, 0.6, 29, 0.95, FAKE, FAKE, FAKE, None, None, FAKE, 1000, None) == 5

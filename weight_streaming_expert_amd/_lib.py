@@ -9,7 +9,7 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwsx.so")
 
-c_void_p, c_int, c_size_t, c_char_p = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_char_p
+c_void_p, c_int, c_size_t, c_char_p, c_float = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_char_p, ctypes.c_float
 
 STATUS = {0: "WSX_OK", 1: "WSX_ERR_NULL", 2: "WSX_ERR_SHAPE", 3: "WSX_ERR_ALIGN", 4: "WSX_ERR_UNSUPPORTED",
           5: "WSX_ERR_WORKSPACE", 6: "WSX_ERR_DTYPE", 7: "WSX_ERR_HIP"}
@@ -43,17 +43,24 @@ _PROTOS = {
                                 c_void_p, c_size_t, c_void_p],
     "lm_head_gemv_bf16_argmax": [c_void_p, c_int, c_int, c_void_p, c_int, c_void_p, c_void_p,
                                  c_void_p, c_size_t, c_void_p],
+    "lm_sample_topk_topp": [c_void_p, c_int, c_int, c_float, c_int, c_float, c_void_p, c_void_p, c_void_p, c_void_p,
+                            c_void_p, c_size_t, c_void_p],
+    "lm_head_gemv_fp8_sample": [c_void_p, c_void_p, c_int, c_int, c_void_p, c_int, c_float, c_int, c_float, c_void_p,
+                                c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "moe_decode_step": [c_void_p, c_int, ctypes.POINTER(MoeStack), c_void_p, c_void_p, c_int,
                         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                         c_void_p, c_size_t, c_void_p],
     "wsx_moe_workspace_bytes": [c_int, c_int, c_int, c_int, c_int],
     "wsx_lm_head_workspace_bytes": [c_int, c_int, c_int],
     "wsx_decode_step_workspace_bytes": [c_int, c_int, c_int, c_int, c_int, c_int],
+    "wsx_sample_workspace_bytes": [c_int, c_int, c_int],
+    "wsx_lm_head_sample_workspace_bytes": [c_int, c_int, c_int, c_int],
     "wsx_status_string": [c_int],
     "wsx_build_info": [],
 }
 _RESTYPES = {"wsx_moe_workspace_bytes": c_size_t, "wsx_lm_head_workspace_bytes": c_size_t,
-             "wsx_decode_step_workspace_bytes": c_size_t, "wsx_status_string": c_char_p,
+             "wsx_decode_step_workspace_bytes": c_size_t, "wsx_sample_workspace_bytes": c_size_t,
+             "wsx_lm_head_sample_workspace_bytes": c_size_t, "wsx_status_string": c_char_p,
              "wsx_build_info": c_char_p}
 EXPORTS = tuple(_PROTOS)
 

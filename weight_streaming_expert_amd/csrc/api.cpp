@@ -178,6 +178,56 @@ wsx_status lm_head_gemv_bf16_argmax(const uint16_t* w, int V, int K, const uint1
   return head_common(1, w, nullptr, V, K, x, T, logits, argmax, ws, ws_bytes, stream);
 }
 
+static wsx_status check_sample(const float* logits, int V, int T, float temperature, int top_k, float top_p,
+                               const float* uniforms, const int32_t* token) {
+  if (!logits || !uniforms || !token) return WSX_ERR_NULL;
+  if (V < 1 || T < 1 || top_k < 1 || top_k > V) return WSX_ERR_SHAPE;
+  if (!(temperature > 0.f) || !(temperature <= 3.0e38f) || !(top_p > 0.f) || !(top_p <= 1.f)) return WSX_ERR_SHAPE;
+  if (T > WSX_MAX_T || !sample_shape_supported(V, top_k)) return WSX_ERR_UNSUPPORTED;
+  return WSX_OK;
+}
+
+size_t wsx_sample_workspace_bytes(int T, int V, int top_k) {
+  if (T < 1 || T > WSX_MAX_T || !sample_shape_supported(V, top_k)) return 0;
+  return sample_ws_bytes(T, V, top_k);
+}
+
+wsx_status lm_sample_topk_topp(const float* logits, int V, int T, float temperature, int top_k, float top_p,
+                               const float* uniforms, int32_t* token, int32_t* topk_ids, float* topk_probs, void* ws,
+                               size_t ws_bytes, void* stream) {
+  wsx_status st = check_sample(logits, V, T, temperature, top_k, top_p, uniforms, token);
+  if (st != WSX_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, sample_ws_bytes(T, V, top_k))) != WSX_OK) return st;
+  return hip_status(launch_sample(logits, V, T, temperature, top_k, top_p, uniforms, token, topk_ids, topk_probs,
+                                  ws, S(stream)));
+}
+
+size_t wsx_lm_head_sample_workspace_bytes(int T, int V, int K, int top_k) {
+  const size_t s = wsx_sample_workspace_bytes(T, V, top_k);
+  return s ? align256(head_ws_bytes()) + 256 + s : 0;
+}
+
+wsx_status lm_head_gemv_fp8_sample(const uint8_t* q, const float* row_scale, int V, int K, const uint16_t* x, int T,
+                                   float temperature, int top_k, float top_p, const float* uniforms, float* logits,
+                                   int32_t* token, int32_t* topk_ids, float* topk_probs, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  if (!q || !row_scale || !x) return WSX_ERR_NULL;
+  wsx_status st = check_sample(logits, V, T, temperature, top_k, top_p, uniforms, token);
+  if (st != WSX_OK) return st;
+  if (K < 32 || K % 32) return WSX_ERR_SHAPE;
+  if (!head_shape_supported(0, K)) return WSX_ERR_UNSUPPORTED;
+  if (!a16(q) || !a16(x)) return WSX_ERR_ALIGN;
+  // workspace: the head's region, 256 bytes for the head's greedy argmax (a
+  // by-product here), then the sampler's candidates
+  const size_t head = align256(head_ws_bytes());
+  if ((st = check_ws(ws, ws_bytes, head + 256 + sample_ws_bytes(T, V, top_k))) != WSX_OK) return st;
+  int32_t* argmax = reinterpret_cast<int32_t*>((char*)ws + head);
+  hipError_t e = launch_lm_head(0, q, row_scale, V, K, x, T, 0, nullptr, logits, argmax, ws, S(stream));
+  if (e != hipSuccess) return WSX_ERR_HIP;
+  return hip_status(launch_sample(logits, V, T, temperature, top_k, top_p, uniforms, token, topk_ids, topk_probs,
+                                  (char*)ws + head + 256, S(stream)));
+}
+
 wsx_status moe_decode_step(const uint16_t* h_in, int T, const wsx_moe_stack* sk, const uint8_t* head_q,
                            const float* head_scale, int V, uint16_t* h_out, float* logits, int32_t* argmax,
                            uint16_t* h_trace, uint16_t* u_trace, int32_t* ids_trace, float* w_trace, void* ws,

@@ -1,0 +1,245 @@
+// Temperature / top-k / top-p sampling of one token per row of the LM head's
+// logits, on gfx950: the sampling epilogue of the head.
+//
+// [ncij] "What happens on a real workload?": the GSM8K run samples with
+// temperature 0.6, top_p 0.95 and top_k 29.  The pages name only the three
+// settings; the steps taken are: keep the top_k logits by (value desc, id
+// asc); e_i = exp((z_i - z_0) / temperature); c_i the running sum in rank
+// order; keep ranks 0..m, m the first with c_m >= top_p * c_{k-1}; p_i =
+// e_i / c_m; the token is the first rank j <= m with c_j > u * c_m (m if
+// none), u being the caller's uniform for that row.  That arithmetic is
+// binary32 in this order.
+//
+// Two launches, both small next to the head itself:
+//  1. candidates: one wavefront per 64-logit chunk, grid (ceil(V / 256), T).
+//     Each lane forms the 64-bit rank key of its logit (order-preserving value
+//     bits over the complemented id, so one unsigned compare orders by value,
+//     ties to the lower id), ranks it against the other 63 keys broadcast by
+//     readlane, and the lanes of rank < k write the chunk's top k to the
+//     workspace; slots past a short chunk get key 0, below every finite
+//     logit's key.
+//  2. selection: one 1024-thread workgroup per row.  The k-th largest chunk
+//     maximum tau (a radix select over the key bytes, stopping once one key
+//     matches) bounds the k-th largest logit from below, so every global
+//     top-k key is a candidate >= tau of one of the (at most k) chunks whose
+//     maximum is >= tau: only those k * k candidates are read, in one round
+//     of loads.  Ranking the survivors against each other gives the top k in
+//     order; one lane then runs the sequential sums and the draw.
+#include "wsx_device.h"
+#include "wsx_internal.h"
+
+namespace wsx {
+
+constexpr int kSampChunk = 64;          // logits per chunk: one wavefront
+constexpr int kSampMaxK = 64;
+constexpr int kSampMaxChunks = 8192;    // V <= 8191 * 64; also bounds the k * k survivors
+
+__global__ void __launch_bounds__(256) sample_candidates_kernel(const float* __restrict__ logits, int V, int k,
+                                                               int nchunk, RankKey* __restrict__ cand) {
+  const int lane = threadIdx.x & 63;
+  const int c = blockIdx.x * 4 + (threadIdx.x >> 6), t = blockIdx.y;
+  if (c >= nchunk) return;   // whole wavefronts leave together
+  const int v = c * kSampChunk + lane;
+  const RankKey mine = v < V ? rank_key(logits[(size_t)t * V + v], v) : 0ull;
+  // rank within the chunk: every other lane's key broadcast through readlane
+  const unsigned hi = (unsigned)(mine >> 32), lo = (unsigned)mine;
+  int r = 0;
+#pragma unroll
+  for (int j = 0; j < 64; ++j) {
+    const RankKey o = ((RankKey)(unsigned)__builtin_amdgcn_readlane((int)hi, j) << 32) |
+                      (unsigned)__builtin_amdgcn_readlane((int)lo, j);
+    r += (int)(o > mine);
+  }
+  RankKey* out = cand + ((size_t)t * nchunk + c) * k;
+  if (mine != 0ull && r < k) out[r] = mine;
+  const int nvalid = min(kSampChunk, V - c * kSampChunk);
+  if (lane >= nvalid && lane < k) out[lane] = 0ull;
+}
+
+// rank of m among buf[0..n) (n even; keys are distinct apart from zeros)
+__device__ __forceinline__ int lds_rank(const RankKey* buf, int n, RankKey m) {
+  int r = 0;
+  for (int j = 0; j < n; j += 2) {
+    const ulonglong2 kk = *reinterpret_cast<const ulonglong2*>(buf + j);
+    r += (int)(kk.x > m) + (int)(kk.y > m);
+  }
+  return r;
+}
+
+__global__ void __launch_bounds__(1024) sample_select_kernel(const RankKey* __restrict__ cand, int nchunk, int k,
+                                                            float temperature, float top_p,
+                                                            const float* __restrict__ uniforms,
+                                                            int32_t* __restrict__ token, int32_t* __restrict__ topk_ids,
+                                                            float* __restrict__ topk_probs) {
+  __shared__ __attribute__((aligned(16))) RankKey buf[kSampMaxChunks];
+  __shared__ RankKey top[kSampMaxK];
+  __shared__ float ev[kSampMaxK];
+  __shared__ float cs_m;
+  __shared__ int qlist[kSampMaxK];
+  __shared__ unsigned hist[256];
+  __shared__ RankKey tau;
+  __shared__ int ns, nq, msel, sel_digit, sel_need, sel_count;
+  const int t = blockIdx.x;
+  const RankKey* ct = cand + (size_t)t * nchunk * k;
+  if (threadIdx.x == 0) {
+    tau = 1ull;   // no cut when there are fewer than k chunks
+    ns = 0;
+    nq = 0;
+  }
+  // every chunk maximum (one load per thread)
+  for (int c = threadIdx.x; c < nchunk; c += blockDim.x) buf[c] = ct[(size_t)c * k];
+  __syncthreads();
+  if (nchunk >= k) {
+    // tau = the k-th largest maximum, by radix select: eight passes over the
+    // key bytes from the top, each a histogram of the keys that match the
+    // digits chosen so far and a scan by one wavefront for the byte that holds
+    // the k-th largest (the maxima are distinct, so the result is one key)
+    RankKey prefix = 0ull, mask = 0ull;
+    int need = k;
+    bool found = false;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+      if (threadIdx.x < 256) hist[threadIdx.x] = 0u;
+      __syncthreads();
+      for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
+        const RankKey key = buf[c];
+        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (threadIdx.x < 64) {
+        // lane l holds bins 255 - 4l .. 252 - 4l: digits in descending order
+        const int lane = threadIdx.x;
+        unsigned h[4], sum = 0u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          h[q] = hist[255 - 4 * lane - q];
+          sum += h[q];
+        }
+        unsigned incl = sum;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const unsigned v = __shfl_up(incl, d, 64);
+          if (lane >= d) incl += v;
+        }
+        unsigned run = incl - sum;   // keys in higher digits
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (run < (unsigned)need && (unsigned)need <= run + h[q]) {
+            sel_digit = 255 - 4 * lane - q;
+            sel_need = need - (int)run;
+            sel_count = (int)h[q];
+          }
+          run += h[q];
+        }
+      }
+      __syncthreads();
+      prefix |= (RankKey)sel_digit << shift;
+      mask |= (RankKey)255u << shift;
+      need = sel_need;
+      if (sel_count == 1) {
+        // one key has these leading digits: it is the k-th largest
+        for (int c = threadIdx.x; c < nchunk; c += blockDim.x)
+          if ((buf[c] & mask) == prefix) tau = buf[c];
+        found = true;
+        break;
+      }
+      __syncthreads();   // every thread has read the choice before the next pass
+    }
+    // the distinct maxima leave one match by the last byte at the latest
+    if (!found && threadIdx.x == 0) tau = prefix;
+  }
+  __syncthreads();
+  const RankKey th = tau;
+  // the chunks whose maximum is >= tau: exactly k of them when there are at
+  // least k chunks (distinct maxima), else all nchunk < k
+  for (int c = threadIdx.x; c < nchunk; c += blockDim.x)
+    if (buf[c] >= th) {
+      const int pos = atomicAdd(&nq, 1);
+      if (pos < kSampMaxK) qlist[pos] = c;
+    }
+  __syncthreads();   // buf is reused for the survivors below
+  // their candidates (<= k * k <= 4096 keys): all loads issued at once
+  const int nload = min(nq, kSampMaxK) * k;
+  RankKey kv[kSampMaxK * kSampMaxK / 1024];
+#pragma unroll
+  for (int r = 0; r < kSampMaxK * kSampMaxK / 1024; ++r) {
+    const int i = threadIdx.x + r * 1024;
+    kv[r] = i < nload ? ct[(size_t)qlist[i / k] * k + i % k] : 0ull;
+  }
+#pragma unroll
+  for (int r = 0; r < kSampMaxK * kSampMaxK / 1024; ++r)
+    if (kv[r] != 0ull && kv[r] >= th) {
+      const int pos = atomicAdd(&ns, 1);
+      if (pos < kSampMaxChunks) buf[pos] = kv[r];
+    }
+  __syncthreads();
+  const int n = min(ns, kSampMaxChunks);
+  if (threadIdx.x == 0 && (n & 1)) buf[n] = 0ull;
+  __syncthreads();
+  const int n2 = (n + 1) & ~1;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const RankKey m = buf[i];
+    const int r = lds_rank(buf, n2, m);
+    if (r < k) top[r] = m;
+  }
+  __syncthreads();
+  const float z0 = key_value(top[0]);
+  if ((int)threadIdx.x < k) ev[threadIdx.x] = expf((key_value(top[threadIdx.x]) - z0) / temperature);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    // the running sums in rank order, held in registers (k <= 64)
+    float c[kSampMaxK];
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < kSampMaxK; ++i) {
+      if (i < k) acc += ev[i];
+      c[i] = acc;
+    }
+    const float thr = top_p * acc;
+    int m = k - 1;
+#pragma unroll
+    for (int i = kSampMaxK - 1; i >= 0; --i)
+      if (i < k && c[i] >= thr) m = i;   // the first such i
+    float mass = c[0];
+#pragma unroll
+    for (int i = 1; i < kSampMaxK; ++i)
+      if (i == m) mass = c[i];
+    const float target = uniforms[t] * mass;
+    int j = m;
+#pragma unroll
+    for (int i = kSampMaxK - 1; i >= 0; --i)
+      if (i <= m && c[i] > target) j = i;   // the first such i
+    msel = m;
+    cs_m = mass;
+    token[t] = key_id(top[j]);
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < k) {
+    const int i = threadIdx.x, m = msel;
+    if (topk_ids) topk_ids[(size_t)t * k + i] = key_id(top[i]);
+    if (topk_probs) topk_probs[(size_t)t * k + i] = i <= m ? ev[i] / cs_m : 0.f;
+  }
+}
+
+size_t sample_ws_bytes(int T, int V, int k) {
+  const size_t nchunk = ((size_t)V + kSampChunk - 1) / kSampChunk;
+  return (size_t)T * nchunk * (size_t)k * sizeof(RankKey);
+}
+
+bool sample_shape_supported(int V, int k) {
+  return V >= 1 && k >= 1 && k <= kSampMaxK && k <= V && (V + kSampChunk - 1) / kSampChunk <= kSampMaxChunks - 1;
+}
+
+hipError_t launch_sample(const float* logits, int V, int T, float temperature, int k, float top_p,
+                         const float* uniforms, int32_t* token, int32_t* topk_ids, float* topk_probs, void* ws,
+                         hipStream_t st) {
+  const int nchunk = (V + kSampChunk - 1) / kSampChunk;
+  RankKey* cand = reinterpret_cast<RankKey*>(ws);
+  sample_candidates_kernel<<<dim3((nchunk + 3) / 4, T), 256, 0, st>>>(logits, V, k, nchunk, cand);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  sample_select_kernel<<<T, 1024, 0, st>>>(cand, nchunk, k, temperature, top_p, uniforms, token, topk_ids,
+                                           topk_probs);
+  return hipGetLastError();
+}
+
+}  // namespace wsx

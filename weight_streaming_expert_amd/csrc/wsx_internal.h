@@ -49,4 +49,11 @@ hipError_t launch_fused_step(const wsx_moe_stack* sk, const uint16_t* h_in, cons
 // lm_head_quant.hip
 hipError_t launch_quant_fp8(const uint16_t* w, int V, int K, uint8_t* q, float* s, hipStream_t st);
 
+// sample.hip: temperature / top-k / top-p sampling of the head's logits
+size_t sample_ws_bytes(int T, int V, int k);
+bool sample_shape_supported(int V, int k);
+hipError_t launch_sample(const float* logits, int V, int T, float temperature, int k, float top_p,
+                         const float* uniforms, int32_t* token, int32_t* topk_ids, float* topk_probs, void* ws,
+                         hipStream_t st);
+
 }  // namespace wsx

@@ -63,6 +63,12 @@ def normal_bf16(key, shape, std):
     return _to_bf16_bits(normal_f32(key, shape, std))
 
 
+def uniform_f32(key, shape):
+    """Draws in [0, 1) as float32 (the sampler's per-token uniforms)."""
+    u = rng(*key).random(size=shape, dtype=np.float32)
+    return np.minimum(u, np.nextafter(np.float32(1), np.float32(0))).astype(np.float32)
+
+
 # ----------------------------------------------------------------------------- MoE weights
 
 

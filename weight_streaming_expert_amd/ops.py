@@ -164,6 +164,48 @@ def lm_head_gemv_bf16_argmax(w, x, want_logits=True, ws=None):
     return logits, am
 
 
+def _sample_args(T, k, uniforms, dev):
+    _chk(uniforms, torch.float32, "uniforms")
+    if uniforms.numel() != T:
+        raise ValueError("uniforms must hold one value per row")
+    tok = torch.empty((T,), dtype=torch.int32, device=dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    probs = torch.empty((T, k), dtype=torch.float32, device=dev)
+    return tok, ids, probs
+
+
+def lm_sample_topk_topp(logits, temperature, top_k, top_p, uniforms, ws=None):
+    """One token per row of logits float32 [T][V]: temperature, top-k, top-p,
+    inverse-CDF draw with uniforms float32 [T].  Returns (token int32 [T],
+    ranked top-k ids int32 [T][k], kept probabilities float32 [T][k])."""
+    _chk(logits, torch.float32, "logits")
+    T, V = logits.shape
+    dev = logits.device
+    tok, ids, probs = _sample_args(T, top_k, uniforms, dev)
+    if ws is None:
+        ws = workspace(max(int(_lib.load().wsx_sample_workspace_bytes(T, V, top_k)), 256), dev)
+    _lib.call("lm_sample_topk_topp", _p(logits), V, T, float(temperature), int(top_k), float(top_p), _p(uniforms),
+              _p(tok), _p(ids), _p(probs), _p(ws), ws.numel(), _stream(dev))
+    return tok, ids, probs
+
+
+def lm_head_gemv_fp8_sample(q, row_scale, x, temperature, top_k, top_p, uniforms, ws=None):
+    """FP8 head then the sampler on its logits.  Returns (logits, token, ids, probs)."""
+    _chk(q, torch.uint8, "q")
+    _chk(row_scale, torch.float32, "row_scale")
+    _chk(x, torch.bfloat16, "x")
+    V, K = q.shape
+    T = x.shape[0]
+    dev = x.device
+    logits = torch.empty((T, V), dtype=torch.float32, device=dev)
+    tok, ids, probs = _sample_args(T, top_k, uniforms, dev)
+    if ws is None:
+        ws = workspace(max(int(_lib.load().wsx_lm_head_sample_workspace_bytes(T, V, K, top_k)), 256), dev)
+    _lib.call("lm_head_gemv_fp8_sample", _p(q), _p(row_scale), V, K, _p(x), T, float(temperature), int(top_k),
+              float(top_p), _p(uniforms), _p(logits), _p(tok), _p(ids), _p(probs), _p(ws), ws.numel(), _stream(dev))
+    return logits, tok, ids, probs
+
+
 class Fp8LmHead:
     """The FP8 head as one object: codes, row scales and shape travel together,
     so FP8 bytes can only ever reach the FP8 GEMV entry point."""
