@@ -139,11 +139,11 @@ def test_sample_argument_errors():
     assert sample(V=8191 * 64 + 1) == 4 and sample(V=8191 * 64, k=64, wsb=0) == 5   # largest V passes the shape checks
     assert sample(ws=None) == 5 and sample(ws=MIS) == 3
     need = lib.wsx_sample_workspace_bytes(1, 157184, 29)
-    assert need == 2456 * 29 * 8            # 64-logit chunks
+    assert need == 2456 * (29 + 1) * 8      # 64-logit chunks: k candidates and the maximum each
     assert sample(wsb=need - 1) == 5
     assert lib.wsx_sample_workspace_bytes(1, 10, 11) == 0
     head_need = lib.wsx_lm_head_sample_workspace_bytes(4, 157184, 2560, 29)
-    assert head_need == lib.wsx_lm_head_workspace_bytes(4, 157184, 2560) + 256 + 4 * 2456 * 29 * 8
+    assert head_need == lib.wsx_lm_head_workspace_bytes(4, 157184, 2560) + 256 + 4 * 2456 * 30 * 8
     f = lib.lm_head_gemv_fp8_sample
     assert f(None, FAKE, 157184, 2560, FAKE, 1, 0.6, 29, 0.95, FAKE, FAKE, FAKE, None, None, FAKE, head_need, None) == 1
     assert f(FAKE, FAKE, 157184, 2560, FAKE, 1, 0.6, 29, 0.95, FAKE, None, FAKE, None, None, FAKE, head_need, None) == 1

@@ -35,7 +35,8 @@ constexpr int kSampMaxK = 64;
 constexpr int kSampMaxChunks = 8192;    // V <= 8191 * 64; also bounds the k * k survivors
 
 __global__ void __launch_bounds__(256) sample_candidates_kernel(const float* __restrict__ logits, int V, int k,
-                                                               int nchunk, RankKey* __restrict__ cand) {
+                                                               int nchunk, RankKey* __restrict__ cand,
+                                                               RankKey* __restrict__ maxima) {
   const int lane = threadIdx.x & 63;
   const int c = blockIdx.x * 4 + (threadIdx.x >> 6), t = blockIdx.y;
   if (c >= nchunk) return;   // whole wavefronts leave together
@@ -52,6 +53,7 @@ __global__ void __launch_bounds__(256) sample_candidates_kernel(const float* __r
   }
   RankKey* out = cand + ((size_t)t * nchunk + c) * k;
   if (mine != 0ull && r < k) out[r] = mine;
+  if (mine != 0ull && r == 0) maxima[(size_t)t * nchunk + c] = mine;   // also packed, for the threshold
   const int nvalid = min(kSampChunk, V - c * kSampChunk);
   if (lane >= nvalid && lane < k) out[lane] = 0ull;
 }
@@ -66,7 +68,8 @@ __device__ __forceinline__ int lds_rank(const RankKey* buf, int n, RankKey m) {
   return r;
 }
 
-__global__ void __launch_bounds__(1024) sample_select_kernel(const RankKey* __restrict__ cand, int nchunk, int k,
+__global__ void __launch_bounds__(1024) sample_select_kernel(const RankKey* __restrict__ cand,
+                                                            const RankKey* __restrict__ maxima, int nchunk, int k,
                                                             float temperature, float top_p,
                                                             const float* __restrict__ uniforms,
                                                             int32_t* __restrict__ token, int32_t* __restrict__ topk_ids,
@@ -81,13 +84,14 @@ __global__ void __launch_bounds__(1024) sample_select_kernel(const RankKey* __re
   __shared__ int ns, nq, msel, sel_digit, sel_need, sel_count;
   const int t = blockIdx.x;
   const RankKey* ct = cand + (size_t)t * nchunk * k;
+  const float u = threadIdx.x == 0 ? uniforms[t] : 0.f;   // in flight from the start
   if (threadIdx.x == 0) {
     tau = 1ull;   // no cut when there are fewer than k chunks
     ns = 0;
     nq = 0;
   }
-  // every chunk maximum (one load per thread)
-  for (int c = threadIdx.x; c < nchunk; c += blockDim.x) buf[c] = ct[(size_t)c * k];
+  // every chunk maximum, from the packed copy
+  for (int c = threadIdx.x; c < nchunk; c += blockDim.x) buf[c] = maxima[(size_t)t * nchunk + c];
   __syncthreads();
   if (nchunk >= k) {
     // tau = the k-th largest maximum, by radix select: eight passes over the
@@ -203,7 +207,7 @@ __global__ void __launch_bounds__(1024) sample_select_kernel(const RankKey* __re
 #pragma unroll
     for (int i = 1; i < kSampMaxK; ++i)
       if (i == m) mass = c[i];
-    const float target = uniforms[t] * mass;
+    const float target = u * mass;
     int j = m;
 #pragma unroll
     for (int i = kSampMaxK - 1; i >= 0; --i)
@@ -222,7 +226,7 @@ __global__ void __launch_bounds__(1024) sample_select_kernel(const RankKey* __re
 
 size_t sample_ws_bytes(int T, int V, int k) {
   const size_t nchunk = ((size_t)V + kSampChunk - 1) / kSampChunk;
-  return (size_t)T * nchunk * (size_t)k * sizeof(RankKey);
+  return (size_t)T * nchunk * ((size_t)k + 1) * sizeof(RankKey);   // candidates, then the packed maxima
 }
 
 bool sample_shape_supported(int V, int k) {
@@ -234,10 +238,11 @@ hipError_t launch_sample(const float* logits, int V, int T, float temperature, i
                          hipStream_t st) {
   const int nchunk = (V + kSampChunk - 1) / kSampChunk;
   RankKey* cand = reinterpret_cast<RankKey*>(ws);
-  sample_candidates_kernel<<<dim3((nchunk + 3) / 4, T), 256, 0, st>>>(logits, V, k, nchunk, cand);
+  RankKey* maxima = cand + (size_t)T * nchunk * k;
+  sample_candidates_kernel<<<dim3((nchunk + 3) / 4, T), 256, 0, st>>>(logits, V, k, nchunk, cand, maxima);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  sample_select_kernel<<<T, 1024, 0, st>>>(cand, nchunk, k, temperature, top_p, uniforms, token, topk_ids,
+  sample_select_kernel<<<T, 1024, 0, st>>>(cand, maxima, nchunk, k, temperature, top_p, uniforms, token, topk_ids,
                                            topk_probs);
   return hipGetLastError();
 }
