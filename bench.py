@@ -14,7 +14,8 @@ Prints one JSON line (rank 0) with the µs per step, the achieved HBM rate of
 the step's algorithmic bytes, the roofline object of the dominant kernel (the
 single-launch decode step), the standalone FP8 head kernel's rate, a
 per-component breakdown (one MoE layer with a cold cache, the FP8 and BF16
-heads, the 4-token verify pass, the load-time quantizer) and the CPU-oracle
+heads, the 4-token verify pass, the sampling epilogue at the GSM8K settings,
+the load-time quantizer) and the CPU-oracle
 baseline timed on a bounded sample of the same workload.
 """
 
