@@ -322,7 +322,7 @@ const char* wsx_build_info(void) {
   return "libwsx arch=gfx950 hip=" WSX_STR(HIP_VERSION_MAJOR) "." WSX_STR(HIP_VERSION_MINOR)
          " kernels=decode_step<T1;one-launch>,router_topk<bf16|f32,T1-4;rank-count>,"
          "moe_gateup<T1;valu-dot2|T2-4;mfma-bf16>,moe_down<T1;valu|T2-4;grouped>,"
-         "lm_head<fp8|bf16,T1;wide-per-CU>,lm_head<fp8,T2-4;mfma-bf16>,lm_head<bf16,T2-4>,quant_fp8";
+         "lm_head<fp8|bf16,T1;wide-per-CU>,lm_head<fp8,T2-4;mfma-bf16>,lm_head<bf16,T2-4>,quant_fp8,sample<topk<=64,topp>";
 }
 
 }  // extern "C"

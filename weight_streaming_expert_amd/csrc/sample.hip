@@ -94,10 +94,11 @@ __global__ void __launch_bounds__(1024) sample_select_kernel(const RankKey* __re
   for (int c = threadIdx.x; c < nchunk; c += blockDim.x) buf[c] = maxima[(size_t)t * nchunk + c];
   __syncthreads();
   if (nchunk >= k) {
-    // tau = the k-th largest maximum, by radix select: eight passes over the
-    // key bytes from the top, each a histogram of the keys that match the
+    // tau = the k-th largest maximum, by radix select: up to eight passes over
+    // the key bytes from the top, each a histogram of the keys that match the
     // digits chosen so far and a scan by one wavefront for the byte that holds
-    // the k-th largest (the maxima are distinct, so the result is one key)
+    // the k-th largest, stopping once a single key matches (the maxima are
+    // distinct, so the result is one key)
     RankKey prefix = 0ull, mask = 0ull;
     int need = k;
     bool found = false;
