@@ -681,7 +681,6 @@ __global__ void __launch_bounds__(256) router_topk_kernel(
   __shared__ TopkScratch R;
   __shared__ int sel_id[WSX_MAX_T * WSX_MAX_K];
   __shared__ float sel_w[WSX_MAX_T * WSX_MAX_K];
-  __shared__ int sel_first[WSX_MAX_T * WSX_MAX_K];
   __shared__ float sw_tab[WSX_MAX_T * WSX_MAX_K * WSX_MAX_T];
 #pragma unroll 1
   for (int t = 0; t < T; ++t) {
@@ -709,22 +708,23 @@ __global__ void __launch_bounds__(256) router_topk_kernel(
   }
   const int n = T * k;
   if (wave == 0) {
-    int id = (lane < n) ? sel_id[lane] : 0x7FFFFFFF;
+    // lane j < n holds selection j (token j / k); the distinct ids and their
+    // ascending slots come from registers: readlane broadcasts, a ballot of
+    // the first occurrences, and a count of the smaller distinct ids
+    constexpr int NS = WSX_MAX_T * WSX_MAX_K;   // n <= NS <= 64
+    const int id = (lane < n) ? sel_id[lane] : 0x7FFFFFFF;
     int first = lane < n;
-    for (int j = 0; j < n; ++j) if (j < lane && sel_id[j] == id) first = 0;
-    if (lane < n) sel_first[lane] = first;
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+      if (j < lane && __builtin_amdgcn_readlane(id, j) == id) first = 0;
+    const unsigned long long fm = __ballot(first);
+    int rank = 0;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) rank += (int)(((fm >> j) & 1ull) != 0 && __builtin_amdgcn_readlane(id, j) < id);
+    if (lane == 0) expert_list[0] = __popcll(fm);
+    if (lane < n && first) expert_list[1 + rank] = id;
+    // the zeros are stored before the weights (one wavefront, in order)
     for (int e = lane; e < n * T; e += 64) sw_tab[e] = 0.f;
-  }
-  __syncthreads();
-  if (wave == 0) {
-    int id = (lane < n) ? sel_id[lane] : 0x7FFFFFFF;
-    int rank = 0, n_active = 0;
-    for (int j = 0; j < n; ++j) {
-      rank += (sel_first[j] && sel_id[j] < id);
-      n_active += sel_first[j];
-    }
-    if (lane == 0) expert_list[0] = n_active;
-    if (lane < n && sel_first[lane]) expert_list[1 + rank] = id;
     if (lane < n) sw_tab[rank * T + lane / k] = sel_w[lane];
   }
   __syncthreads();
