@@ -614,6 +614,71 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ lrow, int E
   __syncthreads();
 }
 
+// Top-k of one token's E logits (E <= 64 PW, k <= 8) by one wavefront, in
+// registers.  Lane l holds logits PW l .. PW l + PW - 1 as 64-bit rank keys
+// (order-preserving value bits over the complemented id, so one unsigned
+// compare orders by value, then lower id; positions past E get key 0).  A
+// logit beaten by the maxima of k other lanes is beaten by k logits, so the
+// top k lie in the k lanes whose maxima rank highest.  Those lanes' keys go
+// to this wavefront's LDS slots (rank-major, zeros elsewhere), and each of the
+// 8 PW candidates is ranked against the others through readlane broadcasts.
+// Leaves the k (logit, id) pairs in rank order in rv / rid.
+__device__ __forceinline__ RankKey readlane_key(RankKey v, int j) {
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(v >> 32), j);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)v, j);
+  return ((RankKey)hi << 32) | lo;
+}
+
+template <int PW>
+__device__ __forceinline__ void wave_topk(const float* __restrict__ lrow, int E, int k, RankKey* cand, float* rv,
+                                          int* rid) {
+  constexpr int NC = 8 * PW;                  // candidate slots: 8 lanes x PW
+  constexpr int CPL = (NC + 63) / 64;         // candidates per lane
+  const int lane = threadIdx.x & 63;
+  RankKey key[PW];
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const int e = PW * lane + i;
+    key[i] = e < E ? rank_key(ld_dev(lrow + e), e) : 0ull;
+  }
+  RankKey mx = key[0];
+#pragma unroll
+  for (int i = 1; i < PW; ++i) mx = key[i] > mx ? key[i] : mx;
+  int r = 0;
+#pragma unroll
+  for (int j = 0; j < 64; ++j) r += (int)(readlane_key(mx, j) > mx);
+#pragma unroll
+  for (int m = 0; m < CPL; ++m)
+    if (lane + 64 * m < NC) cand[lane + 64 * m] = 0ull;
+  __builtin_amdgcn_wave_barrier();
+  if (r < k) {
+#pragma unroll
+    for (int i = 0; i < PW; ++i) cand[r * PW + i] = key[i];
+  }
+  __builtin_amdgcn_wave_barrier();
+  RankKey cv[CPL];
+#pragma unroll
+  for (int m = 0; m < CPL; ++m) cv[m] = lane + 64 * m < NC ? cand[lane + 64 * m] : 0ull;
+  int rk[CPL];
+#pragma unroll
+  for (int m = 0; m < CPL; ++m) rk[m] = 0;
+#pragma unroll
+  for (int m2 = 0; m2 < CPL; ++m2)
+#pragma unroll
+    for (int j = 0; j < 64; ++j) {
+      const RankKey o = readlane_key(cv[m2], j);
+#pragma unroll
+      for (int m = 0; m < CPL; ++m) rk[m] += (int)(o > cv[m]);
+    }
+#pragma unroll
+  for (int m = 0; m < CPL; ++m)
+    if (cv[m] != 0ull && rk[m] < k) {
+      rv[rk[m]] = key_value(cv[m]);
+      rid[rk[m]] = key_id(cv[m]);
+    }
+  __builtin_amdgcn_wave_barrier();
+}
+
 // Router GEMV with one row per wavefront (64 lanes; lane l takes the 16-byte
 // granules l, l + 64, ...; RGPL per lane) for T tokens staged in LDS (and
 // normalized there when `norm` is set).  Every row uses the same lanes and the
@@ -677,35 +742,52 @@ __global__ void __launch_bounds__(256) router_topk_kernel(
   }
   if (!last_block_arrived(counter, gridDim.x, &flag)) return;
 
-  // ---- last workgroup
+  // ---- last workgroup: the top-k and the softmax over the selected logits
+  // in rank order, per token; one token takes the whole workgroup, several
+  // take one wavefront each, side by side
   __shared__ TopkScratch R;
+  __shared__ RankKey wcand[WSX_MAX_T][8 * 4 * P];
+  __shared__ float wrv[WSX_MAX_T][WSX_MAX_K];
+  __shared__ int wrid[WSX_MAX_T][WSX_MAX_K];
   __shared__ int sel_id[WSX_MAX_T * WSX_MAX_K];
   __shared__ float sel_w[WSX_MAX_T * WSX_MAX_K];
   __shared__ float sw_tab[WSX_MAX_T * WSX_MAX_K * WSX_MAX_T];
-#pragma unroll 1
-  for (int t = 0; t < T; ++t) {
-    block_topk<P>(logits + (size_t)t * E, E, k, &R);
-    if (threadIdx.x < k) {
-      const int j0 = threadIdx.x;
-      const float top = R.rv[0];
-      float zs = 0.f, mine = 0.f;
-#pragma unroll
-      for (int j = 0; j < WSX_MAX_K; ++j) {
-        if (j < k) {
-          const float z = __expf(R.rv[j] - top);
-          zs += z;
-          if (j == j0) mine = z;
-        }
-      }
-      const float wj = mine / zs;
-      const int id = R.rid[j0];
-      topk_ids[t * k + j0] = id;
-      topk_w[t * k + j0] = wj;
-      sel_id[t * k + j0] = id;
-      sel_w[t * k + j0] = wj;
+  const float* rv_t;
+  const int* rid_t;
+  int t = 0, j0 = -1;
+  if constexpr (T == 1) {
+    block_topk<P>(logits, E, k, &R);
+    rv_t = R.rv;
+    rid_t = R.rid;
+    if (threadIdx.x < k) j0 = threadIdx.x;
+  } else {
+    t = wave;
+    if (wave < T) {
+      wave_topk<4 * P>(logits + (size_t)t * E, E, k, wcand[t], wrv[t], wrid[t]);
+      if (lane < k) j0 = lane;
     }
-    __syncthreads();
+    rv_t = wrv[t < T ? t : 0];
+    rid_t = wrid[t < T ? t : 0];
   }
+  if (j0 >= 0) {
+    const float top = rv_t[0];
+    float zs = 0.f, mine = 0.f;
+#pragma unroll
+    for (int j = 0; j < WSX_MAX_K; ++j) {
+      if (j < k) {
+        const float z = __expf(rv_t[j] - top);
+        zs += z;
+        if (j == j0) mine = z;
+      }
+    }
+    const float wj = mine / zs;
+    const int id = rid_t[j0];
+    topk_ids[t * k + j0] = id;
+    topk_w[t * k + j0] = wj;
+    sel_id[t * k + j0] = id;
+    sel_w[t * k + j0] = wj;
+  }
+  __syncthreads();
   const int n = T * k;
   if (wave == 0) {
     // lane j < n holds selection j (token j / k); the distinct ids and their
