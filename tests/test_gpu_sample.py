@@ -152,6 +152,24 @@ def test_fused_exact_integer_head(ops):
         check_row(ref[t], 2.0, 64, 0.9, float(u[t]), int(P.np_(tok)[t]), P.np_(ids)[t], P.np_(probs)[t])
 
 
+@pytest.mark.parametrize("V,K,T", [(4099, 256, 1), (4099, 256, 3), (1000, 2560, 2), (65, 2560, 1)])
+def test_fused_ragged_heads(ops, V, K, T):
+    """The fused entry on other head instances (K = 256, the 2-4 row paths):
+    its logits against the head oracle, its ids, probabilities and token
+    against the sampling oracle on those logits."""
+    w = inputs.normal_bf16((31, V, K), (V, K), 0.02)
+    q, s = ops.lm_head_quantize_fp8(P.to_dev_bf16(w))
+    x = inputs.normal_bf16((32, V, K, T), (T, K), 1.0)
+    u = inputs.uniform_f32((33, V, K, T), (T,))
+    k = min(64, V)
+    logits, tok, ids, probs = ops.lm_head_gemv_fp8_sample(q, s, P.to_dev_bf16(x), 1.3, k, 0.5, P.to_dev(u))
+    lg = P.np_(logits)
+    ok, worst = C.fp_close(lg, OH.head_logits(P.np_(q), P.np_(s), x))
+    assert ok, worst
+    for t in range(T):
+        check_row(lg[t], 1.3, k, 0.5, float(u[t]), int(P.np_(tok)[t]), P.np_(ids)[t], P.np_(probs)[t])
+
+
 def test_sampler_is_deterministic(ops):
     z = inputs.normal_f32((29,), (4, 157184), 3.0)
     u = inputs.uniform_f32((30,), (4,))
