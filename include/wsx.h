@@ -24,9 +24,13 @@
  *    returns WSX_ERR_HIP.  The library never aborts or prints.
  *  - Workspaces: `ws` is caller-allocated device memory of at least the size
  *    returned by the matching *_workspace_bytes query, 256-byte aligned, and
- *    ZERO-FILLED BEFORE ITS FIRST USE.  Counters inside it return to zero at
- *    the end of every call, so it is reusable without clearing.  Calls that
- *    may run concurrently (different streams) need distinct workspaces.
+ *    ZERO-FILLED BEFORE ITS FIRST USE.  Counters and error words inside it
+ *    return to zero at the end of every call, so it is reusable without
+ *    clearing (moe_decode_step also keeps a step counter there that advances
+ *    by one per call).  A workspace may be reused with any T; a decode-step
+ *    workspace serves one stack shape (H, I, E, k, V) and must be zero-filled
+ *    again before it is used with another.  Calls that may run concurrently
+ *    (different streams) need distinct workspaces.
  *  - Inputs must be finite and must not contain the E8M0 byte 0xFF (NaN);
  *    otherwise results are unspecified but the call still completes.
  *  - Reductions use a fixed order, so repeated calls give bit-identical
@@ -167,6 +171,10 @@ wsx_status lm_head_gemv_fp8_argmax(const uint8_t* q, const float* row_scale, int
  * lm_head_gemv_bf16_argmax — the unquantized BF16 head, the 2x-bytes
  * comparison for the FP8 head.  Same contract as lm_head_gemv_fp8_argmax
  * without row scales: logits[t][v] = sum_k w[v][k] * x[t][k].
+ *
+ * [saipien] "Why one user waits on weights" and "Stop hauling the vocabulary
+ * in full precision": before the FP8 head, the 157,184 x 2,560 projection was
+ * read in full precision for every token.
  */
 wsx_status lm_head_gemv_bf16_argmax(const uint16_t* w, int V, int K, const uint16_t* x, int T,
                                     float* logits, int32_t* argmax, void* ws, size_t ws_bytes,
@@ -239,6 +247,12 @@ typedef struct wsx_moe_stack {
  * moe_decode_step — one decode (T = 1) or MTP-verify (T <= 4) pass through L
  * stacked MoE layers and the FP8 LM head, with no host synchronization.
  *
+ * [saipien] "Why one user waits on weights": a batch-1 decode step streams,
+ * for every layer, the router, 8 of 512 routed experts and the shared expert,
+ * then the whole vocabulary projection; [saipien] "Stop hauling the
+ * vocabulary in full precision" for the FP8 head; [saipien] "Draft three
+ * tokens, verify four" for the 4-position verify pass.
+ *
  * For l = 0..L-1:  u_l = RNE_bf16(h_l / sqrt(mean(h_l^2) + 1e-6))   (per token)
  *                  h_{l+1} = moe layer l on input u_l with residual h_l
  * then logits = FP8 head applied to u_L, argmax as lm_head_gemv_fp8_argmax.
@@ -248,6 +262,12 @@ typedef struct wsx_moe_stack {
  *
  * h_in bf16 [T][H]; h_out bf16 [T][H] (the final residual stream);
  * logits float [T][V] or NULL; argmax int32 [T].
+ * Failure report: at T = 1 with a compiled shape (see wsx_build_info) the
+ * whole step is one launch whose workgroups wait on each other with bounded
+ * waits.  If a wait gives up (it never should), the step still completes,
+ * argmax[0] is -1 and h_out / logits are unspecified; the error does not
+ * carry over, so the next call on the same workspace runs normally.  The
+ * return status only reports host-side checks and launch errors.
  * Optional traces (each NULL or the full size): h_trace bf16 [L+1][T][H]
  * (h_0..h_L), u_trace bf16 [L+1][T][H] (u_0..u_L, u_L being the head input),
  * ids_trace int32 [L][T][k], w_trace float [L][T][k].
@@ -258,6 +278,17 @@ wsx_status moe_decode_step(const uint16_t* h_in, int T, const wsx_moe_stack* sta
                            uint16_t* h_out, float* logits, int32_t* argmax,
                            uint16_t* h_trace, uint16_t* u_trace, int32_t* ids_trace, float* w_trace,
                            void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * wsx_read_probe — measurement utility, not a step of the decode path: one
+ * plain streaming read of `bytes` bytes at `buf` (16-byte loads, all issued
+ * before use), the reference rate for "how fast can weights come out of
+ * memory" ([ncij] "Why is MoE decoding on DGX Spark memory-bound?").
+ * `out` (one uint32) receives an XOR of what was read, so the reads cannot be
+ * optimized away; its value has no meaning.
+ * Limits: bytes > 0 and a multiple of 16, buf 16-byte aligned.
+ */
+wsx_status wsx_read_probe(const void* buf, size_t bytes, uint32_t* out, void* stream);
 
 size_t wsx_moe_workspace_bytes(int T, int H, int I, int E, int k);
 size_t wsx_lm_head_workspace_bytes(int T, int V, int K);

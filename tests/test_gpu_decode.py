@@ -188,3 +188,38 @@ def test_same_workspace_decode_and_verify_passes(ops):
         h0 = inputs.normal_bf16((wl.seed, 55, step), (T, H), 1.0)
         out = ops.moe_decode_step(P.to_dev_bf16(h0), stack, head, trace=True, ws=ws)
         check_step(wl, layers, out, qh, sh, h0)
+
+
+@pytest.mark.parametrize("shape", ["ling", "tiny"])
+def test_failed_wait_reports_minus_one_and_does_not_carry_over(ops, ling_stack, shape):
+    """The one-launch step's failure report, forced from the host.  The step's
+    error word (workspace bytes 256..259: the line after the 256-byte epoch
+    line) is preset to the tag base of the next step, (epoch + 1) << 8.  Every
+    wait of that step then gives up within 16 polls, every workgroup still runs
+    to its end, and the step reports argmax -1.  The error word is clear
+    afterwards, the epoch has advanced, and the next step on the same workspace
+    gives the normal result bit for bit."""
+    if shape == "ling":
+        wl, layers, stack, head, qh, sh = ling_stack
+    else:
+        wl = configs.TINY
+        layers, stack = build_stack(ops, wl, 2)
+        head = ops.Fp8LmHead.quantize(P.to_dev_bf16(inputs.head_weights(wl, K=wl.moe.H)))
+    m = wl.moe
+    ws = ops.workspace(ops.decode_step_workspace_bytes(1, m.H, m.I, m.E, m.k, head.V), "cuda")
+    x = P.to_dev_bf16(inputs.normal_bf16((wl.seed, 91), (1, m.H), 1.0))
+    ref = ops.moe_decode_step(x, stack, head, ws=ws)
+    torch.cuda.synchronize()
+    assert int(ref["argmax"][0]) >= 0
+    ref = {key: v.clone() for key, v in ref.items()}
+    ctl = ws[:512].view(torch.int32)
+    epoch = int(ctl[0])
+    ctl[64] = (epoch + 1) << 8
+    bad = ops.moe_decode_step(x, stack, head, ws=ws)
+    torch.cuda.synchronize()
+    assert int(bad["argmax"][0]) == -1
+    assert int(ctl[64]) == 0 and int(ctl[0]) == epoch + 1
+    again = ops.moe_decode_step(x, stack, head, ws=ws)
+    torch.cuda.synchronize()
+    for key in ("h", "logits", "argmax"):
+        assert torch.equal(again[key], ref[key]), key

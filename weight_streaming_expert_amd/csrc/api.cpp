@@ -17,22 +17,27 @@ inline hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
 inline wsx_status hip_status(hipError_t e) { return e == hipSuccess ? WSX_OK : WSX_ERR_HIP; }
 
 struct MoeWs {
-  size_t counter, logits, a, part, dcnt, total;
+  size_t counter, dcnt, logits, a, part, total;
 };
-// counter (router), router logits, expert activations, then the grouped down
-// kernel's partial sums and its per-row-tile counters (64-byte stride)
+// The counters first, at offsets that depend on H only, so one workspace
+// serves calls with any T (every counter is back at zero after a call): the
+// router's counter, the grouped down kernel's per-row-tile counters (64-byte
+// stride); then the router logits, the expert activations and the grouped
+// down kernel's partial sums, all overwritten before they are read.
 MoeWs moe_ws(int T, int H, int I, int E, int k) {
   MoeWs w;
   w.counter = 0;
-  w.logits = 256;
+  w.dcnt = 256;
+  w.logits = align256(w.dcnt + (size_t)(H / 32 + 1) * 64);
   w.a = align256(w.logits + (size_t)T * E * 4);
   w.part = align256(w.a + (size_t)(T * k + 1) * T * I * 4);
-  w.dcnt = align256(w.part + (size_t)down_groups(T * k + 1) * T * H * 4);
-  w.total = align256(w.dcnt + (size_t)(H / 32 + 1) * 64);
+  w.total = align256(w.part + (size_t)down_groups(T * k + 1) * T * H * 4);
   return w;
 }
 size_t head_ws_bytes() { return 256 + (size_t)2 * kHeadMaxGrid * WSX_MAX_T * 4; }
 
+// The per-phase region of the decode step: the head's region (its counter
+// first) and the MoE region at fixed offsets, then the T-dependent buffers.
 struct StepWs {
   MoeWs moe;
   size_t moe_base, head, u, h0, h1, ids, w, el, sw, total;
@@ -40,9 +45,9 @@ struct StepWs {
 StepWs step_ws(int T, int H, int I, int E, int k) {
   StepWs s;
   s.moe = moe_ws(T, H, I, E, k);
-  s.moe_base = 0;
-  s.head = align256(s.moe.total);
-  s.u = align256(s.head + head_ws_bytes());
+  s.head = 0;
+  s.moe_base = align256(head_ws_bytes());
+  s.u = align256(s.moe_base + s.moe.total);
   s.h0 = align256(s.u + (size_t)T * H * 2);
   s.h1 = align256(s.h0 + (size_t)T * H * 2);
   s.ids = align256(s.h1 + (size_t)T * H * 2);
@@ -92,6 +97,26 @@ wsx_status check_experts(const uint16_t* x, const uint8_t* w13c, const uint8_t* 
   return WSX_OK;
 }
 
+// The host-side checks of moe_decode_step that do not involve the workspace.
+wsx_status moe_decode_step_check(const uint16_t* h_in, int T, const wsx_moe_stack* sk, const uint8_t* head_q,
+                                 const float* head_scale, int V, const uint16_t* h_out, const int32_t* argmax,
+                                 const uint16_t* h_trace, const uint16_t* u_trace) {
+  if (!sk || !h_in || !head_q || !head_scale || !h_out || !argmax) return WSX_ERR_NULL;
+  if (sk->L < 1) return WSX_ERR_SHAPE;
+  if (sk->L > WSX_MAX_LAYERS - 1) return WSX_ERR_UNSUPPORTED;
+  const int H = sk->H, I = sk->I, E = sk->E, k = sk->k;
+  wsx_status st = check_router(h_in, sk->w_router, sk->router_dtype, T, H, E, k);
+  if (st != WSX_OK) return st;
+  st = check_experts(h_in, sk->w13_codes, sk->w13_scales, sk->w2_codes, sk->w2_scales, sk->sh13_codes,
+                     sk->sh13_scales, sk->sh2_codes, sk->sh2_scales, T, H, I, E, k);
+  if (st != WSX_OK) return st;
+  if (V < 1) return WSX_ERR_SHAPE;
+  if (!head_shape_supported(0, H)) return WSX_ERR_UNSUPPORTED;
+  if (!a16(head_q) || !a16(h_out)) return WSX_ERR_ALIGN;
+  if ((h_trace && !a16(h_trace)) || (u_trace && !a16(u_trace))) return WSX_ERR_ALIGN;
+  return WSX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -119,7 +144,7 @@ wsx_status moe_route_topk(const uint16_t* x, const void* w_router, int router_dt
   wsx_status st = check_router(x, w_router, router_dtype, T, H, E, k);
   if (st != WSX_OK) return st;
   if (!topk_ids || !topk_w || !expert_list || !slot_w) return WSX_ERR_NULL;
-  if ((st = check_ws(ws, ws_bytes, moe_ws(T, H, 32, E, k).a)) != WSX_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, moe_ws(T, H, 32, E, k).a)) != WSX_OK) return st;   // counters + logits
   const MoeWs L = moe_ws(T, H, 32, E, k);
   float* logits = logits_out ? logits_out : reinterpret_cast<float*>((char*)ws + L.logits);
   return hip_status(launch_router(router_dtype, w_router, E, H, k, x, T, 0, nullptr, logits, topk_ids, topk_w,
@@ -232,19 +257,9 @@ wsx_status moe_decode_step(const uint16_t* h_in, int T, const wsx_moe_stack* sk,
                            const float* head_scale, int V, uint16_t* h_out, float* logits, int32_t* argmax,
                            uint16_t* h_trace, uint16_t* u_trace, int32_t* ids_trace, float* w_trace, void* ws,
                            size_t ws_bytes, void* stream) {
-  if (!sk || !h_in || !head_q || !head_scale || !h_out || !argmax) return WSX_ERR_NULL;
-  if (sk->L < 1) return WSX_ERR_SHAPE;
-  if (sk->L > WSX_MAX_LAYERS - 1) return WSX_ERR_UNSUPPORTED;
+  wsx_status st = moe_decode_step_check(h_in, T, sk, head_q, head_scale, V, h_out, argmax, h_trace, u_trace);
+  if (st != WSX_OK) return st;
   const int H = sk->H, I = sk->I, E = sk->E, k = sk->k, L = sk->L;
-  wsx_status st = check_router(h_in, sk->w_router, sk->router_dtype, T, H, E, k);
-  if (st != WSX_OK) return st;
-  st = check_experts(h_in, sk->w13_codes, sk->w13_scales, sk->w2_codes, sk->w2_scales, sk->sh13_codes,
-                     sk->sh13_scales, sk->sh2_codes, sk->sh2_scales, T, H, I, E, k);
-  if (st != WSX_OK) return st;
-  if (V < 1) return WSX_ERR_SHAPE;
-  if (!head_shape_supported(0, H)) return WSX_ERR_UNSUPPORTED;
-  if (!a16(head_q) || !a16(h_out)) return WSX_ERR_ALIGN;
-  if ((h_trace && !a16(h_trace)) || (u_trace && !a16(u_trace))) return WSX_ERR_ALIGN;
   const StepWs W = step_ws(T, H, I, E, k);
   // workspace: the single-launch step's exchange buffers first (their place
   // does not depend on T), then the per-phase region
@@ -255,11 +270,12 @@ wsx_status moe_decode_step(const uint16_t* h_in, int T, const wsx_moe_stack* sk,
                                         ids_trace, w_trace, ws, S(stream), kStepSegments));
 
   char* base = reinterpret_cast<char*>(ws) + fused_bytes;
-  unsigned* counter = reinterpret_cast<unsigned*>(base + W.moe.counter);
-  float* rlogits = reinterpret_cast<float*>(base + W.moe.logits);
-  float* a = reinterpret_cast<float*>(base + W.moe.a);
-  float* part = reinterpret_cast<float*>(base + W.moe.part);
-  unsigned* dcnt = reinterpret_cast<unsigned*>(base + W.moe.dcnt);
+  char* mbase = base + W.moe_base;
+  unsigned* counter = reinterpret_cast<unsigned*>(mbase + W.moe.counter);
+  float* rlogits = reinterpret_cast<float*>(mbase + W.moe.logits);
+  float* a = reinterpret_cast<float*>(mbase + W.moe.a);
+  float* part = reinterpret_cast<float*>(mbase + W.moe.part);
+  unsigned* dcnt = reinterpret_cast<unsigned*>(mbase + W.moe.dcnt);
   int32_t* el = reinterpret_cast<int32_t*>(base + W.el);
   float* sw = reinterpret_cast<float*>(base + W.sw);
   uint16_t* ping[2] = {reinterpret_cast<uint16_t*>(base + W.h0), reinterpret_cast<uint16_t*>(base + W.h1)};
@@ -300,6 +316,13 @@ wsx_status moe_decode_step(const uint16_t* h_in, int T, const wsx_moe_stack* sk,
   uint16_t* u_head = u_trace ? u_trace + (size_t)L * TH : nullptr;
   return hip_status(launch_lm_head(0, head_q, head_scale, V, H, h_cur, T, 1, u_head, logits, argmax,
                                    base + W.head, s));
+}
+
+wsx_status wsx_read_probe(const void* buf, size_t bytes, uint32_t* out, void* stream) {
+  if (!buf || !out) return WSX_ERR_NULL;
+  if (bytes == 0 || bytes % 16) return WSX_ERR_SHAPE;
+  if (!a16(buf)) return WSX_ERR_ALIGN;
+  return hip_status(launch_read_probe(buf, bytes, out, S(stream)));
 }
 
 const char* wsx_status_string(wsx_status s) {

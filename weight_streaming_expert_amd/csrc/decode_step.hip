@@ -21,8 +21,10 @@
 // A workgroup only ever waits for data produced by workgroups with a LOWER
 // index.  Workgroups are dispatched in index order, so the lowest-indexed
 // unfinished workgroup never waits for anything unfinished, and the grid
-// always drains.  Every wait is also bounded: on timeout it raises an error
-// word, all later waits return at once and the step reports argmax = -1.
+// always drains.  Every wait is also bounded: on timeout it raises the step's
+// error word, the step's later waits return at once and the step reports
+// argmax = -1.  The error word holds the failed step's tag base, so it never
+// affects another step, and the step's last workgroup clears it.
 //
 // Data crosses workgroups only through device-coherent (sc1) stores and loads,
 // performed at the device coherence point, and every exchanged value travels
@@ -101,9 +103,17 @@ struct FusedStepArgs {
 namespace {
 
 __device__ __forceinline__ Ctl* ctl(const FusedStepArgs& A) { return reinterpret_cast<Ctl*>(A.b.ctl); }
-__device__ __forceinline__ void raise_err(const FusedStepArgs& A) { st_dev(reinterpret_cast<int*>(&ctl(A)->err), 1); }
-__device__ __forceinline__ bool err_set(const FusedStepArgs& A) {
-  return ld_dev(reinterpret_cast<const int*>(&ctl(A)->err)) != 0;
+// The error word of a step holds that step's tag base ((epoch + 1) << 8, never
+// zero), taken from any of the step's tags.  It is raised before the raising
+// workgroup stores anything else (the store is acknowledged first), so every
+// workgroup that later sees one of its outputs also sees the error.
+__device__ __forceinline__ unsigned err_word(unsigned tag) { return tag & ~0xFFu; }
+__device__ __forceinline__ void raise_err(const FusedStepArgs& A, unsigned tag) {
+  st_dev(reinterpret_cast<int*>(&ctl(A)->err), (int)err_word(tag));
+  wait_vmem();
+}
+__device__ __forceinline__ bool err_set(const FusedStepArgs& A, unsigned tag) {
+  return (unsigned)ld_dev(reinterpret_cast<const int*>(&ctl(A)->err)) == err_word(tag);
 }
 
 // LDS layouts of the normalized activations, chosen so that the 8 lanes a
@@ -135,23 +145,14 @@ __device__ __forceinline__ int my_copy(int copies) { return (int)(blockIdx.x % c
 
 // ---------------------------------------------------------------- waits
 
-// Whole-workgroup decision to stop waiting: the wait has run too long, or
-// another wait already failed.  Thread 0 decides for everyone.
-__device__ __forceinline__ bool block_should_bail(const FusedStepArgs& A, int it) {
-  int bail = 0;
-  if (threadIdx.x == 0) {
-    if (it >= kSpinMax) { raise_err(A); bail = 1; }
-    else if ((it & 15) == 15 && err_set(A)) bail = 1;
-  }
-  return __syncthreads_or(bail) != 0;
-}
-
-// The same for one wavefront (lane 0 decides).
-__device__ __forceinline__ bool wave_should_bail(const FusedStepArgs& A, int it) {
+// Wavefront decision to stop waiting for data carrying `tag`: the wait has run
+// too long, or another wait of the same step already failed.  Lane 0 decides
+// for the wavefront.
+__device__ __forceinline__ bool wave_should_bail(const FusedStepArgs& A, int it, unsigned tag) {
   int bail = 0;
   if ((threadIdx.x & 63) == 0) {
-    if (it >= kSpinMax) { raise_err(A); bail = 1; }
-    else if ((it & 15) == 15 && err_set(A)) bail = 1;
+    if (it >= kSpinMax) { raise_err(A, tag); bail = 1; }
+    else if ((it & 15) == 15 && err_set(A, tag)) bail = 1;
   }
   return __shfl(bail, 0) != 0;
 }
@@ -162,7 +163,7 @@ __device__ __forceinline__ bool wave_should_bail(const FusedStepArgs& A, int it)
 __device__ __forceinline__ void sleep_on_tag(const FusedStepArgs& A, const uint2* p, int index, unsigned want) {
   for (int it = 0; it < kSpinMax; ++it) {
     if (ld_coh4(p, (uint32_t)index * 8 + 4) == want) return;
-    if ((it & 15) == 15 && err_set(A)) return;
+    if ((it & 15) == 15 && err_set(A, want)) return;
     __builtin_amdgcn_s_sleep(8);
   }
 }
@@ -196,7 +197,7 @@ __device__ __forceinline__ void wait_u(const FusedStepArgs& A, int l, unsigned t
       }
     }
     if (__all(pend == 0)) break;
-    if (wave_should_bail(A, it)) break;
+    if (wave_should_bail(A, it, tag)) break;
     __builtin_amdgcn_s_sleep(1);
   }
   float ss = 0.f;
@@ -358,7 +359,7 @@ __device__ __forceinline__ void route_topk(const FusedStepArgs& A, unsigned tag,
       ok = (w.y == tag) & (w.w == tag);
     }
     if (__all(ok)) break;
-    if (wave_should_bail(A, it)) break;
+    if (wave_should_bail(A, it, tag)) break;
     __builtin_amdgcn_s_sleep(1);
   }
   const RankKey k0 = rank_key(v0, e0), k1 = rank_key(v1, e0 + 1);
@@ -587,7 +588,7 @@ __device__ __forceinline__ void wave_wait_slot(const FusedStepArgs& A, int s, un
       }
     }
     if (__all(pend == 0)) break;
-    if (wave_should_bail(A, it)) break;
+    if (wave_should_bail(A, it, tag)) break;
     __builtin_amdgcn_s_sleep(1);
   }
 }
@@ -645,7 +646,7 @@ __device__ __forceinline__ void wave_routed_dots(const FusedStepArgs& A, unsigne
       }
     }
     if (!todo) break;
-    if (wave_should_bail(A, it)) break;
+    if (wave_should_bail(A, it, tag)) break;
     __builtin_amdgcn_s_sleep(1);
   }
 }
@@ -763,10 +764,10 @@ __device__ __forceinline__ void role_down(const FusedStepArgs& A, int l, int d, 
       uint2 p = make_uint2(0, 0);
       for (int it = 0; it < kSpinMax; ++it) {
         p = ld_coh8(hx_buf(A, l, my_copy(kCopiesH)), (uint32_t)(n >> 1) * 8);
-        if (p.y == base + l - 1 || ((it & 15) == 15 && err_set(A))) break;
+        if (p.y == base + l - 1 || ((it & 15) == 15 && err_set(A, base))) break;
         __builtin_amdgcn_s_sleep(1);
       }
-      if (p.y != base + l - 1) raise_err(A);
+      if (p.y != base + l - 1) raise_err(A, base);
       res = bf16_bits_to_f32((n & 1) ? (p.x >> 16) : (p.x & 0xFFFFu));
     }
     part[4 * kDRows + threadIdx.x] = res;
@@ -896,13 +897,18 @@ __device__ __forceinline__ void role_head(const FusedStepArgs& A, int hb, unsign
     const RankKey key = (v == v) ? rank_key(v, i) : 0ull;   // a NaN never wins
     __hip_atomic_fetch_max(&ctl(A)->best, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  // the last workgroup to arrive reads the maximum, publishes the argmax,
-  // clears the maximum and advances the epoch for the next step
+  // the last workgroup to arrive reads the maximum, publishes the argmax
+  // (-1 if a wait of this step gave up), clears the maximum and the error
+  // word, and advances the epoch for the next step.  Every other workgroup of
+  // the step has passed all of its waits by now (each one's last store feeds
+  // the head), so none can raise the error after this point.
   if (!last_block_arrived(&ctl(A)->top_counter, A.n_head, flag)) return;
   if (threadIdx.x == 0) {
     const RankKey best = __hip_atomic_load(&ctl(A)->best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(&ctl(A)->best, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    A.argmax[0] = (err_set(A) || best == 0ull) ? -1 : key_id(best);
+    const bool failed = err_set(A, base);
+    A.argmax[0] = (failed || best == 0ull) ? -1 : key_id(best);
+    st_dev(reinterpret_cast<int*>(&ctl(A)->err), 0);
     const unsigned ep = (unsigned)ld_dev(reinterpret_cast<const int*>(&ctl(A)->epoch));
     st_dev(reinterpret_cast<int*>(&ctl(A)->epoch), (int)((ep + 1) % kEpochMod));
   }

@@ -46,6 +46,9 @@ hipError_t launch_fused_step(const wsx_moe_stack* sk, const uint16_t* h_in, cons
                              uint16_t* h_out, float* logits, int32_t* argmax, uint16_t* h_trace, uint16_t* u_trace,
                              int32_t* ids_trace, float* w_trace, void* ws, hipStream_t st, int segments);
 
+// probe.hip: plain streaming read of a buffer (bandwidth reference)
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* out, hipStream_t st);
+
 // lm_head_quant.hip
 hipError_t launch_quant_fp8(const uint16_t* w, int V, int K, uint8_t* q, float* s, hipStream_t st);
 
