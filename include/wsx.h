@@ -290,6 +290,29 @@ wsx_status moe_decode_step(const uint16_t* h_in, int T, const wsx_moe_stack* sta
  */
 wsx_status wsx_read_probe(const void* buf, size_t bytes, uint32_t* out, void* stream);
 
+/*
+ * moe_decode_step_noalloc — moe_decode_step without a workspace argument, for
+ * callers that cannot allocate device memory (code under graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  It allocates nothing: its
+ * workspace is a static device array of WSX_NOALLOC_SCRATCH_BYTES held by each
+ * GPU the library runs on until the process ends.
+ *
+ * Same arguments, results and failure report as moe_decode_step.  Shapes
+ * whose decode-step workspace (wsx_decode_step_workspace_bytes) exceeds
+ * WSX_NOALLOC_SCRATCH_BYTES return WSX_ERR_WORKSPACE before anything is
+ * enqueued.  On the first call on a device, and whenever the stack shape
+ * (H, I, E, k, V) differs from the previous call's on that device, the array
+ * is cleared by a kernel enqueued on `stream` ahead of the step.  Every call
+ * on one GPU shares that GPU's array: calls that overlap on one GPU (different
+ * streams, or host threads) race and give unspecified results.
+ */
+#define WSX_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+wsx_status moe_decode_step_noalloc(const uint16_t* h_in, int T, const wsx_moe_stack* stack,
+                                   const uint8_t* head_q, const float* head_scale, int V,
+                                   uint16_t* h_out, float* logits, int32_t* argmax,
+                                   uint16_t* h_trace, uint16_t* u_trace, int32_t* ids_trace,
+                                   float* w_trace, void* stream);
+
 size_t wsx_moe_workspace_bytes(int T, int H, int I, int E, int k);
 size_t wsx_lm_head_workspace_bytes(int T, int V, int K);
 size_t wsx_decode_step_workspace_bytes(int T, int H, int I, int E, int k, int V);

@@ -149,3 +149,21 @@ def test_sample_argument_errors():
     assert f(FAKE, FAKE, 157184, 2560, FAKE, 1, 0.6, 29, 0.95, FAKE, None, FAKE, None, None, FAKE, head_need, None) == 1
     assert f(FAKE, FAKE, 157184, 100, FAKE, 1, 0.6, 29, 0.95, FAKE, FAKE, FAKE, None, None, FAKE, head_need, None) == 2
     assert f(FAKE, FAKE, 157184, 2560, FAKE, 1, 0.6, 29, 0.95, FAKE, FAKE, FAKE, None, None, FAKE, 1000, None) == 5
+
+
+def test_noalloc_decode_step_rejects_on_the_host():
+    """The allocation-free step checks everything on the host first: a shape
+    whose workspace exceeds the device array is refused, and so are the
+    allocating step's argument errors, before the device is touched."""
+    lib = _lib.load()
+    f = lib.moe_decode_step_noalloc
+    big = _lib.MoeStack(FAKE, 0, FAKE, FAKE, FAKE, FAKE, None, None, None, None, 2, 8192, 2048, 1024, 8)
+    st = _lib.MoeStack(FAKE, 0, FAKE, FAKE, FAKE, FAKE, None, None, None, None, 2, 2560, 768, 512, 8)
+    args = lambda **kw: [kw.get("h", FAKE), kw.get("T", 1), ctypes.byref(kw.get("st", st)), FAKE, FAKE,
+                         kw.get("V", 157184), FAKE, None, FAKE, None, None, None, None, None]
+    assert lib.wsx_decode_step_workspace_bytes(4, 8192, 2048, 1024, 8, 157184) > (4 << 20)
+    assert f(*args(st=big, T=4)) == 5
+    assert f(*args(h=None)) == 1
+    assert f(*args(T=6)) == 4
+    assert f(*args(V=0)) == 2
+    assert f(FAKE, 1, None, FAKE, FAKE, 157184, FAKE, None, FAKE, None, None, None, None, None) == 1

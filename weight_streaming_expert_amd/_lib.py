@@ -50,6 +50,8 @@ _PROTOS = {
     "moe_decode_step": [c_void_p, c_int, ctypes.POINTER(MoeStack), c_void_p, c_void_p, c_int,
                         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                         c_void_p, c_size_t, c_void_p],
+    "moe_decode_step_noalloc": [c_void_p, c_int, ctypes.POINTER(MoeStack), c_void_p, c_void_p, c_int,
+                                c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
     "wsx_read_probe": [c_void_p, c_size_t, c_void_p, c_void_p],
     "wsx_moe_workspace_bytes": [c_int, c_int, c_int, c_int, c_int],
     "wsx_lm_head_workspace_bytes": [c_int, c_int, c_int],

@@ -5,7 +5,15 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "wsx_internal.h"
+
+// Device scratch of the allocation-free decode step (moe_decode_step_noalloc):
+// one copy per GPU, held until the process ends.  Host code never uses this
+// name as an address: each device's copy is located once with
+// hipGetSymbolAddress and only that pointer is passed to kernels.
+static __device__ __align__(256) uint8_t scratch[WSX_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -251,6 +259,71 @@ wsx_status lm_head_gemv_fp8_sample(const uint8_t* q, const float* row_scale, int
   if (e != hipSuccess) return WSX_ERR_HIP;
   return hip_status(launch_sample(logits, V, T, temperature, top_k, top_p, uniforms, token, topk_ids, topk_probs,
                                   (char*)ws + head + 256, S(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Zero fill of the scratch at set-up, as a kernel on the caller's stream.
+__global__ void zero_scratch_kernel(uint4* p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+constexpr int kMaxDevices = 64;
+struct ScratchShape {
+  int H, I, E, k, V;
+  bool operator==(const ScratchShape& o) const { return H == o.H && I == o.I && E == o.E && k == o.k && V == o.V; }
+};
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];          // this device's copy of `scratch`, once located
+ScratchShape g_scratch_shape[kMaxDevices];  // the stack shape its contents belong to
+
+// The current device's scratch pointer for a stack of shape `sh`.  On the
+// first call on a device the symbol is located (hipGetSymbolAddress, with that
+// device current).  The whole array is cleared by a kernel enqueued on `s`,
+// ahead of the step that follows on the same stream, on that first call and
+// whenever the stack shape differs from the previous call's (the layout of
+// the exchange buffers and counters depends on it).
+wsx_status scratch_for_current_device(hipStream_t s, const ScratchShape& sh, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return WSX_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  void* ptr = g_scratch_ptr[dev];
+  const bool fresh = ptr == nullptr;
+  if (fresh && (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)) return WSX_ERR_HIP;
+  if (fresh || !(g_scratch_shape[dev] == sh)) {
+    zero_scratch_kernel<<<256, 256, 0, s>>>(reinterpret_cast<uint4*>(ptr), WSX_NOALLOC_SCRATCH_BYTES / 16);
+    if (hipGetLastError() != hipSuccess) return WSX_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+    g_scratch_shape[dev] = sh;
+  }
+  *out = ptr;
+  return WSX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+wsx_status moe_decode_step_noalloc(const uint16_t* h_in, int T, const wsx_moe_stack* sk, const uint8_t* head_q,
+                                   const float* head_scale, int V, uint16_t* h_out, float* logits, int32_t* argmax,
+                                   uint16_t* h_trace, uint16_t* u_trace, int32_t* ids_trace, float* w_trace,
+                                   void* stream) {
+  if (!sk) return WSX_ERR_NULL;
+  const size_t need = wsx_decode_step_workspace_bytes(T, sk->H, sk->I, sk->E, sk->k, V);
+  if (need == 0) return (T < 1 || sk->k < 1 || sk->E < 1 || V < 0) ? WSX_ERR_SHAPE : WSX_ERR_UNSUPPORTED;
+  if (need > WSX_NOALLOC_SCRATCH_BYTES) return WSX_ERR_WORKSPACE;
+  // every host-side check of the allocating entry point, with a stand-in
+  // workspace, before anything touches the device
+  wsx_status st = moe_decode_step_check(h_in, T, sk, head_q, head_scale, V, h_out, argmax, h_trace, u_trace);
+  if (st != WSX_OK) return st;
+  void* ws = nullptr;
+  if ((st = scratch_for_current_device(S(stream), ScratchShape{sk->H, sk->I, sk->E, sk->k, V}, &ws)) != WSX_OK)
+    return st;
+  return moe_decode_step(h_in, T, sk, head_q, head_scale, V, h_out, logits, argmax, h_trace, u_trace, ids_trace,
+                         w_trace, ws, WSX_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 wsx_status moe_decode_step(const uint16_t* h_in, int T, const wsx_moe_stack* sk, const uint8_t* head_q,
