@@ -20,4 +20,4 @@ Parity status per function is listed in each module header; every function
 here is pinned by a CPU test against something other than itself.
 """
 
-from . import formats, moe, head, compare, sample  # noqa: F401
+from . import formats, moe, head, compare, sample, w4a8  # noqa: F401
