@@ -17,7 +17,8 @@ the step's algorithmic bytes, the roofline object of the dominant kernel (the
 single-launch decode step), the standalone FP8 head kernel's rate, a
 per-component breakdown (one MoE layer over 100 seeded cold inputs, the FP8
 and BF16 heads, the 4-token verify pass, the sampling epilogue at the GSM8K
-settings, the load-time quantizer), a pure-read bandwidth probe, and the
+settings, the load-time quantizer, the W4A8 layer at 1 and 4 tokens), a
+pure-read bandwidth probe, and the
 CPU oracle on three of the timed steps (every layer checked against the
 device, teacher-forced) with its time per step at one BLAS thread and at all
 cores, plus its time per unit of the smaller workloads.
@@ -388,7 +389,11 @@ def breakdown(torch, ops, configs, inputs, dev, stack, head, head_w, wl, quant_u
     # 100 four-token verify passes
     layer = dict(router=stack.w_router[0], w13c=stack.w13_codes[0], w13s=stack.w13_scales[0],
                  w2c=stack.w2_codes[0], w2s=stack.w2_scales[0], shared=tuple(t[0] for t in stack.shared))
-    for wlx, name in ((configs.MOE_LAYER, "moe_layer_t1"), (configs.VERIFY, "moe_layer_verify_t4")):
+    rows = ((configs.MOE_LAYER, "moe_layer_t1", ops.moe_expert_gemv_mxfp4),
+            (configs.VERIFY, "moe_layer_verify_t4", ops.moe_expert_gemv_mxfp4),
+            (configs.MOE_LAYER, "moe_layer_w4a8_t1", ops.moe_expert_gemv_w4a8),
+            (configs.VERIFY, "moe_layer_w4a8_verify_t4", ops.moe_expert_gemv_w4a8))
+    for wlx, name, experts in rows:
         T = wlx.T
         xs = [bf16_dev(inputs.activations(wlx, s)) for s in range(wlx.steps)]
         x = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
@@ -399,8 +404,8 @@ def breakdown(torch, ops, configs, inputs, dev, stack, head, head_w, wl, quant_u
 
         def layer_call():
             rr = ops.moe_route_topk(x, layer["router"], k, ws=ws)
-            ops.moe_expert_gemv_mxfp4(x, layer["w13c"], layer["w13s"], layer["w2c"], layer["w2s"], rr["expert_list"],
-                                      rr["slot_w"], k, shared=layer["shared"], residual=res, ws=ws)
+            experts(x, layer["w13c"], layer["w13s"], layer["w2c"], layer["w2s"], rr["expert_list"], rr["slot_w"], k,
+                    shared=layer["shared"], residual=res, ws=ws)
             held["el"] = rr["expert_list"]
 
         def before(i):
@@ -455,6 +460,7 @@ def breakdown(torch, ops, configs, inputs, dev, stack, head, head_w, wl, quant_u
     t.update(first_call_incl_alloc_us=round(quant_us, 1))
     out["quantize_fp8"] = t
     out["verify_over_decode_layer"] = round(out["moe_layer_verify_t4"]["median_us"] / out["moe_layer_t1"]["median_us"], 3)
+    out["w4a8_over_bf16_layer_t1"] = round(out["moe_layer_w4a8_t1"]["median_us"] / out["moe_layer_t1"]["median_us"], 3)
     del flush_buf
     return out
 

@@ -131,6 +131,49 @@ wsx_status moe_expert_gemv_mxfp4(const uint16_t* x,
                                  void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * act_quantize_mxfp8 — the W4A8 path's activation quantizer: bf16 rows to
+ * MXFP8 with E4M3 elements.
+ *
+ * [saipien] "Why one user waits on weights": the baseline recipe was "W4A8",
+ * which the page reads as 4-bit weights and 8-bit activations.  Per block of
+ * 32 consecutive elements of a row:
+ *   X = floor(log2(max |x|)) - 8, clamped to [-127, 127] (-127 for a zero block)
+ *   codes = E4M3FN_RNE(clamp(x / 2^X, -448, 448)),  scale byte = X + 127
+ *
+ * x bf16 [T][K]; codes uint8 [T][K]; scales uint8 [T][K/32].
+ * Limits: T >= 1, K % 32 == 0.  No workspace.
+ */
+wsx_status act_quantize_mxfp8(const uint16_t* x, int T, int K, uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * moe_expert_gemv_w4a8 — moe_expert_gemv_mxfp4 with 8-bit activations: the
+ * same MXFP4 weights contracted on the matrix cores with MXFP8 activations
+ * ([saipien] "Why one user waits on weights", the W4A8 baseline recipe).
+ *
+ * For each active slot s (expert e) and token t:
+ *   xq = MXFP8(x[t])                       (as act_quantize_mxfp8)
+ *   g = Wg[e] xq, u = Wu[e] xq,  a = silu(g) * u   (fp32)
+ *   aq = MXFP8(a)                          (per 32 values of I, from binary32)
+ *   y[t] = sum_s slot_w[s][t] * (W2[e] aq) + (the shared expert, weight 1)
+ *   out_h[t] = RNE_bf16(residual[t] + y[t])
+ *
+ * Arguments, layouts and limits as moe_expert_gemv_mxfp4, plus act_out:
+ * float [T*k+1][T][I] or NULL, the binary32 a of every slot (slots in list
+ * order, then the shared expert) before its quantization.  Shapes: H and I
+ * multiples of 32, at most 2560 each; T * (H + H/32) <= 65536.
+ * Workspace: wsx_moe_workspace_bytes(T, H, I, E, k).
+ */
+wsx_status moe_expert_gemv_w4a8(const uint16_t* x,
+                                const uint8_t* w13_codes, const uint8_t* w13_scales,
+                                const uint8_t* w2_codes, const uint8_t* w2_scales,
+                                const uint8_t* sh13_codes, const uint8_t* sh13_scales,
+                                const uint8_t* sh2_codes, const uint8_t* sh2_scales,
+                                const int32_t* expert_list, const float* slot_w,
+                                int T, int H, int I, int E, int k,
+                                const uint16_t* residual, float* out_y, uint16_t* out_h, float* act_out,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/*
  * lm_head_quantize_fp8 — load-time BF16 -> FP8 E4M3FN quantization of the
  * vocabulary projection, one fp32 scale per row.
  *

@@ -167,3 +167,21 @@ def test_noalloc_decode_step_rejects_on_the_host():
     assert f(*args(T=6)) == 4
     assert f(*args(V=0)) == 2
     assert f(FAKE, 1, None, FAKE, FAKE, 157184, FAKE, None, FAKE, None, None, None, None, None) == 1
+
+
+def test_w4a8_argument_errors():
+    lib = _lib.load()
+    q = lib.act_quantize_mxfp8
+    assert q(None, 1, 64, FAKE, FAKE, None) == 1
+    assert q(FAKE, 0, 64, FAKE, FAKE, None) == 2
+    assert q(FAKE, 1, 48, FAKE, FAKE, None) == 2
+    assert q(MIS, 1, 64, FAKE, FAKE, None) == 3
+    f = lib.moe_expert_gemv_w4a8
+    args = lambda **kw: [kw.get("x", FAKE), FAKE, FAKE, FAKE, FAKE, None, None, None, None, FAKE, FAKE,
+                         kw.get("T", 1), kw.get("H", 2560), kw.get("I", 768), 512, 8, None, FAKE, None,
+                         kw.get("act", None), kw.get("ws", FAKE), kw.get("wsb", 1 << 26), None]
+    assert f(*args(x=None)) == 1
+    assert f(*args(H=4096)) == 4                 # beyond the W4A8 kernels' 2560
+    assert f(*args(T=6)) == 4
+    assert f(*args(act=MIS)) == 3
+    assert f(*args(wsb=100)) == 5

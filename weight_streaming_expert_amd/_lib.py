@@ -38,6 +38,10 @@ _PROTOS = {
     "moe_expert_gemv_mxfp4": [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                               c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
                               c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
+    "act_quantize_mxfp8": [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p],
+    "moe_expert_gemv_w4a8": [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                             c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
+                             c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "lm_head_quantize_fp8": [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p],
     "lm_head_gemv_fp8_argmax": [c_void_p, c_void_p, c_int, c_int, c_void_p, c_int, c_void_p, c_void_p,
                                 c_void_p, c_size_t, c_void_p],

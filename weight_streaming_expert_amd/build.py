@@ -20,7 +20,7 @@ OUT = os.path.join(HERE, "libwsx.so")
 BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["gemv_rows.hip", "moe_experts.hip", "lm_head_quant.hip", "decode_step.hip", "sample.hip", "probe.hip", "api.cpp"]
+SOURCES = ["gemv_rows.hip", "moe_experts.hip", "moe_w4a8.hip", "lm_head_quant.hip", "decode_step.hip", "sample.hip", "probe.hip", "api.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-x", "hip",

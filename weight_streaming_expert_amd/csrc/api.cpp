@@ -182,6 +182,34 @@ wsx_status moe_expert_gemv_mxfp4(const uint16_t* x, const uint8_t* w13_codes, co
                                 residual, out_y, out_h, nullptr, part, dcnt, S(stream)));
 }
 
+wsx_status act_quantize_mxfp8(const uint16_t* x, int T, int K, uint8_t* codes, uint8_t* scales, void* stream) {
+  if (!x || !codes || !scales) return WSX_ERR_NULL;
+  if (T < 1 || K < 32 || K % 32) return WSX_ERR_SHAPE;
+  if ((size_t)T * (K / 32) > 0x7FFFFFFF) return WSX_ERR_UNSUPPORTED;
+  if (!a16(x) || !a16(codes)) return WSX_ERR_ALIGN;
+  return hip_status(launch_act_quant(x, T, K, codes, scales, S(stream)));
+}
+
+wsx_status moe_expert_gemv_w4a8(const uint16_t* x, const uint8_t* w13_codes, const uint8_t* w13_scales,
+                                const uint8_t* w2_codes, const uint8_t* w2_scales, const uint8_t* sh13_codes,
+                                const uint8_t* sh13_scales, const uint8_t* sh2_codes, const uint8_t* sh2_scales,
+                                const int32_t* expert_list, const float* slot_w, int T, int H, int I, int E, int k,
+                                const uint16_t* residual, float* out_y, uint16_t* out_h, float* act_out, void* ws,
+                                size_t ws_bytes, void* stream) {
+  if (!expert_list || !slot_w) return WSX_ERR_NULL;
+  wsx_status st = check_experts(x, w13_codes, w13_scales, w2_codes, w2_scales, sh13_codes, sh13_scales, sh2_codes,
+                                sh2_scales, T, H, I, E, k);
+  if (st != WSX_OK) return st;
+  if (!w4a8_shape_supported(T, H, I)) return WSX_ERR_UNSUPPORTED;
+  if (out_h && !residual) return WSX_ERR_NULL;
+  if (act_out && !a16(act_out)) return WSX_ERR_ALIGN;
+  const MoeWs L = moe_ws(T, H, I, E, k);
+  if ((st = check_ws(ws, ws_bytes, L.total)) != WSX_OK) return st;
+  return hip_status(launch_w4a8_experts(x, T, H, I, E, k, w13_codes, w13_scales, w2_codes, w2_scales, sh13_codes,
+                                        sh13_scales, sh2_codes, sh2_scales, expert_list, slot_w, residual, out_y,
+                                        out_h, act_out, (char*)ws + L.a, S(stream)));
+}
+
 wsx_status lm_head_quantize_fp8(const uint16_t* w, int V, int K, uint8_t* q, float* row_scale, void* stream) {
   if (!w || !q || !row_scale) return WSX_ERR_NULL;
   if (V < 1 || K < 32 || K % 32) return WSX_ERR_SHAPE;

@@ -39,6 +39,16 @@ hipError_t launch_down(int T, int H, int I, int E, int k, const uint8_t* w2c, co
 int down_groups(int max_slots);
 bool down_grouped_ok(int T, int H, int I);
 
+// moe_w4a8.hip: W4A8 experts (MXFP4 weights x MXFP8 activations on the matrix cores)
+bool w4a8_shape_supported(int T, int H, int I);
+size_t w4a8_act_bytes(int T, int I, int max_slots);
+hipError_t launch_act_quant(const uint16_t* x, int T, int K, uint8_t* codes, uint8_t* scales, hipStream_t st);
+hipError_t launch_w4a8_experts(const uint16_t* x, int T, int H, int I, int E, int k, const uint8_t* w13c,
+                               const uint8_t* w13s, const uint8_t* w2c, const uint8_t* w2s, const uint8_t* sh13c,
+                               const uint8_t* sh13s, const uint8_t* sh2c, const uint8_t* sh2s, const int32_t* el,
+                               const float* sw, const uint16_t* res, float* y, uint16_t* h, float* act, void* abuf,
+                               hipStream_t st);
+
 // decode_step.hip: the whole 1-token decode step in one launch
 bool fused_step_supported(int T, int router_dtype, bool has_shared, int H, int I, int E, int k);
 size_t fused_step_workspace_bytes(int H, int I, int E, int k, int V);

@@ -121,6 +121,41 @@ def moe_expert_gemv_mxfp4(x, w13_codes, w13_scales, w2_codes, w2_scales, expert_
     return y, h
 
 
+def act_quantize_mxfp8(x):
+    """bf16 [T][K] -> (E4M3 codes uint8 [T][K], E8M0 scale bytes uint8 [T][K/32])."""
+    _chk(x, torch.bfloat16, "x")
+    T, K = x.shape
+    codes = torch.empty((T, K), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((T, K // 32), dtype=torch.uint8, device=x.device)
+    _lib.call("act_quantize_mxfp8", _p(x), T, K, _p(codes), _p(scales), _stream(x.device))
+    return codes, scales
+
+
+def moe_expert_gemv_w4a8(x, w13_codes, w13_scales, w2_codes, w2_scales, expert_list, slot_w, k,
+                         shared=None, residual=None, want_y=True, want_h=True, want_act=False, ws=None):
+    """W4A8 routed + shared SwiGLU experts (MXFP8 activations).  Returns
+    (y float32 [T][H] or None, h bf16 [T][H] or None, act float32 [T*k+1][T][I] or None)."""
+    _chk(x, torch.bfloat16, "x")
+    T, H = x.shape
+    E = w13_codes.shape[0]
+    I = w13_codes.shape[1] // 2
+    for name, t in (("w13_codes", w13_codes), ("w13_scales", w13_scales), ("w2_codes", w2_codes), ("w2_scales", w2_scales)):
+        _chk(t, torch.uint8, name)
+    _chk(expert_list, torch.int32, "expert_list")
+    _chk(slot_w, torch.float32, "slot_w")
+    sh = [None] * 4 if shared is None else list(shared)
+    dev = x.device
+    y = torch.empty((T, H), dtype=torch.float32, device=dev) if want_y else None
+    h = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if (want_h and residual is not None) else None
+    act = torch.zeros((T * k + 1, T, I), dtype=torch.float32, device=dev) if want_act else None
+    if ws is None:
+        ws = workspace(moe_workspace_bytes(T, H, I, E, k), dev)
+    _lib.call("moe_expert_gemv_w4a8", _p(x), _p(w13_codes), _p(w13_scales), _p(w2_codes), _p(w2_scales),
+              *[_p(t) for t in sh], _p(expert_list), _p(slot_w), T, H, I, E, k,
+              _p(residual), _p(y), _p(h), _p(act), _p(ws), ws.numel(), _stream(dev))
+    return y, h, act
+
+
 # ----------------------------------------------------------------------------- LM head
 
 
