@@ -17,7 +17,8 @@ the step's algorithmic bytes, the roofline object of the dominant kernel (the
 single-launch decode step), the standalone FP8 head kernel's rate, a
 per-component breakdown (one MoE layer over 100 seeded cold inputs, the FP8
 and BF16 heads, the 4-token verify pass, the sampling epilogue at the GSM8K
-settings, the load-time quantizer, the W4A8 layer at 1 and 4 tokens), a
+settings, the load-time quantizer, the W4A8 layer at 1 and 4 tokens, the
+grouped layer at 16 tokens in bf16 and W4A8), a
 pure-read bandwidth probe, and the
 CPU oracle on three of the timed steps (every layer checked against the
 device, teacher-forced) with its time per step at one BLAS thread and at all
@@ -392,7 +393,9 @@ def breakdown(torch, ops, configs, inputs, dev, stack, head, head_w, wl, quant_u
     rows = ((configs.MOE_LAYER, "moe_layer_t1", ops.moe_expert_gemv_mxfp4),
             (configs.VERIFY, "moe_layer_verify_t4", ops.moe_expert_gemv_mxfp4),
             (configs.MOE_LAYER, "moe_layer_w4a8_t1", ops.moe_expert_gemv_w4a8),
-            (configs.VERIFY, "moe_layer_w4a8_verify_t4", ops.moe_expert_gemv_w4a8))
+            (configs.VERIFY, "moe_layer_w4a8_verify_t4", ops.moe_expert_gemv_w4a8),
+            (configs.GROUPED16, "moe_layer_grouped_t16", ops.moe_expert_gemv_mxfp4),
+            (configs.GROUPED16, "moe_layer_w4a8_grouped_t16", ops.moe_expert_gemv_w4a8))
     for wlx, name, experts in rows:
         T = wlx.T
         xs = [bf16_dev(inputs.activations(wlx, s)) for s in range(wlx.steps)]

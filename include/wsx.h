@@ -59,7 +59,8 @@ typedef enum wsx_status {
 
 enum { WSX_DTYPE_BF16 = 0, WSX_DTYPE_F32 = 1 };
 
-#define WSX_MAX_T 4    /* tokens per pass: 1 = decode, 4 = MTP verify */
+#define WSX_MAX_T 4    /* tokens per pass of the head, the sampler and the decode step: 1 = decode, 4 = MTP verify */
+#define WSX_MAX_T_MOE 16 /* tokens per pass of one MoE layer (router and experts): a small batch or a longer draft */
 #define WSX_MAX_K 8    /* routed experts chosen per token */
 #define WSX_MAX_E 1024 /* routed experts per layer */
 
@@ -85,7 +86,8 @@ enum { WSX_DTYPE_BF16 = 0, WSX_DTYPE_F32 = 1 };
  * topk_ids  int32 [T][k]; topk_w float [T][k]
  * expert_list int32 [1 + T*k]; slot_w float [T*k][T] (rows past n_active are 0)
  * logits_out float [T][E] or NULL
- * Limits: 1 <= T <= 4, 1 <= k <= 8, k <= E <= 1024, H % 32 == 0.
+ * Limits: 1 <= T <= WSX_MAX_T_MOE (16: a small batch or a longer draft),
+ * 1 <= k <= 8, k <= E <= 1024, H % 32 == 0.
  * Workspace: wsx_moe_workspace_bytes(T, H, I, E, k) (any I).
  */
 wsx_status moe_route_topk(const uint16_t* x, const void* w_router, int router_dtype,
@@ -116,8 +118,10 @@ wsx_status moe_route_topk(const uint16_t* x, const void* w_router, int router_dt
  * expert_list, slot_w: as written by moe_route_topk (or built by the caller).
  * residual bf16 [T][H] or NULL; out_y float [T][H] or NULL; out_h bf16 [T][H]
  *          or NULL (requires residual).
- * Limits: 1 <= T <= 4, 1 <= k <= 8, H % 32 == 0, I % 32 == 0, I <= 2048,
- *          H <= 8192.  Ids in expert_list must lie in [0, E).
+ * Each active expert serves the tokens with a nonzero weight in its slot row
+ * (the expert-sorted token lists); the shared expert serves every token.
+ * Limits: 1 <= T <= WSX_MAX_T_MOE (16), 1 <= k <= 8, H % 32 == 0, I % 32 == 0,
+ *          I <= 2048, H <= 8192.  Ids in expert_list must lie in [0, E).
  * Workspace: wsx_moe_workspace_bytes(T, H, I, E, k).
  */
 wsx_status moe_expert_gemv_mxfp4(const uint16_t* x,

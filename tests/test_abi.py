@@ -56,7 +56,7 @@ def test_route_argument_errors():
     assert route(ids=None) == 1
     assert route(dt=7) == 6
     assert route(T=0) == 2
-    assert route(T=5) == 4
+    assert route(T=17) == 4                      # MoE layers take up to 16 tokens
     assert route(k=9) == 4
     assert route(k=0) == 2
     assert route(E=4, k=8) == 2
@@ -80,7 +80,7 @@ def test_expert_argument_errors():
     assert experts(h=FAKE, res=None) == 1
     assert experts(I=100) == 2
     assert experts(H=0) == 2
-    assert experts(T=9) == 4
+    assert experts(T=17) == 4
     assert experts(I=32 * 1000) == 4
     assert experts(c2=MIS) == 3
     assert experts(wsb=100) == 5
@@ -182,6 +182,6 @@ def test_w4a8_argument_errors():
                          kw.get("act", None), kw.get("ws", FAKE), kw.get("wsb", 1 << 26), None]
     assert f(*args(x=None)) == 1
     assert f(*args(H=4096)) == 4                 # beyond the W4A8 kernels' 2560
-    assert f(*args(T=6)) == 4
+    assert f(*args(T=17)) == 4
     assert f(*args(act=MIS)) == 3
     assert f(*args(wsb=100)) == 5

@@ -49,10 +49,12 @@ LM_HEAD = Workload("lm_head_157184x2560_fp8", T=1, V=157184, moe=MoEShape(H=2560
                    steps=100, seed=31)
 # MTP verify: the MoE layer on 4 tokens with independent top-8 routing, then the head on 4 rows.
 VERIFY = Workload("mtp_verify_t4", T=4, moe=LING_MOE, layers=1, V=157184, steps=100, seed=41)
+# A small batch or a longer draft: the MoE layer on 16 tokens with independent top-8 routing.
+GROUPED16 = Workload("moe_layer_grouped_t16", T=16, moe=LING_MOE, layers=1, steps=20, seed=61)
 # Full decode step: 32 stacked MoE layers (512 experts each) then the FP8 head, 2000 seeded tokens.
 DECODE_STEP = Workload("decode_step_32x_moe_fp8_head", T=1, moe=LING_MOE, layers=32, V=157184, steps=2000, seed=51)
 
-ALL = {w.name: w for w in (TINY, MOE_LAYER, LM_HEAD, VERIFY, DECODE_STEP)}
+ALL = {w.name: w for w in (TINY, MOE_LAYER, LM_HEAD, VERIFY, GROUPED16, DECODE_STEP)}
 
 
 def mxfp4_bytes(N, K):

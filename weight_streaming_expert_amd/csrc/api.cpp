@@ -66,9 +66,11 @@ StepWs step_ws(int T, int H, int I, int E, int k) {
   return s;
 }
 
-wsx_status check_tk(int T, int k, int E) {
+// maxT: WSX_MAX_T_MOE for the MoE layer's entry points, WSX_MAX_T where the
+// head or the decode step is involved
+wsx_status check_tk(int T, int k, int E, int maxT) {
   if (T < 1 || k < 1 || E < 1 || k > E) return WSX_ERR_SHAPE;
-  if (T > WSX_MAX_T || k > WSX_MAX_K || E > WSX_MAX_E) return WSX_ERR_UNSUPPORTED;
+  if (T > maxT || k > WSX_MAX_K || E > WSX_MAX_E) return WSX_ERR_UNSUPPORTED;
   return WSX_OK;
 }
 
@@ -79,10 +81,11 @@ wsx_status check_ws(const void* ws, size_t have, size_t need) {
   return WSX_OK;
 }
 
-wsx_status check_router(const uint16_t* x, const void* w_router, int router_dtype, int T, int H, int E, int k) {
+wsx_status check_router(const uint16_t* x, const void* w_router, int router_dtype, int T, int H, int E, int k,
+                        int maxT) {
   if (!x || !w_router) return WSX_ERR_NULL;
   if (router_dtype != WSX_DTYPE_BF16 && router_dtype != WSX_DTYPE_F32) return WSX_ERR_DTYPE;
-  wsx_status st = check_tk(T, k, E);
+  wsx_status st = check_tk(T, k, E, maxT);
   if (st != WSX_OK) return st;
   if (H < 32 || H % 32) return WSX_ERR_SHAPE;
   if (!router_shape_supported(router_dtype, H)) return WSX_ERR_UNSUPPORTED;
@@ -93,11 +96,11 @@ wsx_status check_router(const uint16_t* x, const void* w_router, int router_dtyp
 // Weights and shapes of the expert stage (the expert list is checked by the caller).
 wsx_status check_experts(const uint16_t* x, const uint8_t* w13c, const uint8_t* w13s, const uint8_t* w2c,
                          const uint8_t* w2s, const uint8_t* sh13c, const uint8_t* sh13s, const uint8_t* sh2c,
-                         const uint8_t* sh2s, int T, int H, int I, int E, int k) {
+                         const uint8_t* sh2s, int T, int H, int I, int E, int k, int maxT) {
   if (!x || !w13c || !w13s || !w2c || !w2s) return WSX_ERR_NULL;
   const int nsh = (sh13c != nullptr) + (sh13s != nullptr) + (sh2c != nullptr) + (sh2s != nullptr);
   if (nsh != 0 && nsh != 4) return WSX_ERR_NULL;
-  wsx_status st = check_tk(T, k, E);
+  wsx_status st = check_tk(T, k, E, maxT);
   if (st != WSX_OK) return st;
   if (H < 32 || I < 32 || H % 32 || I % 32) return WSX_ERR_SHAPE;
   if (!experts_shape_supported(H, I)) return WSX_ERR_UNSUPPORTED;
@@ -113,10 +116,10 @@ wsx_status moe_decode_step_check(const uint16_t* h_in, int T, const wsx_moe_stac
   if (sk->L < 1) return WSX_ERR_SHAPE;
   if (sk->L > WSX_MAX_LAYERS - 1) return WSX_ERR_UNSUPPORTED;
   const int H = sk->H, I = sk->I, E = sk->E, k = sk->k;
-  wsx_status st = check_router(h_in, sk->w_router, sk->router_dtype, T, H, E, k);
+  wsx_status st = check_router(h_in, sk->w_router, sk->router_dtype, T, H, E, k, WSX_MAX_T);
   if (st != WSX_OK) return st;
   st = check_experts(h_in, sk->w13_codes, sk->w13_scales, sk->w2_codes, sk->w2_scales, sk->sh13_codes,
-                     sk->sh13_scales, sk->sh2_codes, sk->sh2_scales, T, H, I, E, k);
+                     sk->sh13_scales, sk->sh2_codes, sk->sh2_scales, T, H, I, E, k, WSX_MAX_T);
   if (st != WSX_OK) return st;
   if (V < 1) return WSX_ERR_SHAPE;
   if (!head_shape_supported(0, H)) return WSX_ERR_UNSUPPORTED;
@@ -131,7 +134,7 @@ extern "C" {
 
 size_t wsx_moe_workspace_bytes(int T, int H, int I, int E, int k) {
   (void)H;
-  if (T < 1 || T > WSX_MAX_T || k < 1 || k > WSX_MAX_K || E < 1 || E > WSX_MAX_E || I < 0) return 0;
+  if (T < 1 || T > WSX_MAX_T_MOE || k < 1 || k > WSX_MAX_K || E < 1 || E > WSX_MAX_E || I < 0) return 0;
   return moe_ws(T, H, I, E, k).total;
 }
 
@@ -149,7 +152,7 @@ size_t wsx_decode_step_workspace_bytes(int T, int H, int I, int E, int k, int V)
 wsx_status moe_route_topk(const uint16_t* x, const void* w_router, int router_dtype, int T, int H, int E, int k,
                           int32_t* topk_ids, float* topk_w, int32_t* expert_list, float* slot_w, float* logits_out,
                           void* ws, size_t ws_bytes, void* stream) {
-  wsx_status st = check_router(x, w_router, router_dtype, T, H, E, k);
+  wsx_status st = check_router(x, w_router, router_dtype, T, H, E, k, WSX_MAX_T_MOE);
   if (st != WSX_OK) return st;
   if (!topk_ids || !topk_w || !expert_list || !slot_w) return WSX_ERR_NULL;
   if ((st = check_ws(ws, ws_bytes, moe_ws(T, H, 32, E, k).a)) != WSX_OK) return st;   // counters + logits
@@ -167,7 +170,7 @@ wsx_status moe_expert_gemv_mxfp4(const uint16_t* x, const uint8_t* w13_codes, co
                                  void* stream) {
   if (!expert_list || !slot_w) return WSX_ERR_NULL;
   wsx_status st = check_experts(x, w13_codes, w13_scales, w2_codes, w2_scales, sh13_codes, sh13_scales, sh2_codes,
-                                sh2_scales, T, H, I, E, k);
+                                sh2_scales, T, H, I, E, k, WSX_MAX_T_MOE);
   if (st != WSX_OK) return st;
   if (out_h && !residual) return WSX_ERR_NULL;
   const MoeWs L = moe_ws(T, H, I, E, k);
@@ -198,7 +201,7 @@ wsx_status moe_expert_gemv_w4a8(const uint16_t* x, const uint8_t* w13_codes, con
                                 size_t ws_bytes, void* stream) {
   if (!expert_list || !slot_w) return WSX_ERR_NULL;
   wsx_status st = check_experts(x, w13_codes, w13_scales, w2_codes, w2_scales, sh13_codes, sh13_scales, sh2_codes,
-                                sh2_scales, T, H, I, E, k);
+                                sh2_scales, T, H, I, E, k, WSX_MAX_T_MOE);
   if (st != WSX_OK) return st;
   if (!w4a8_shape_supported(T, H, I)) return WSX_ERR_UNSUPPORTED;
   if (out_h && !residual) return WSX_ERR_NULL;

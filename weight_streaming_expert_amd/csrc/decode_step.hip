@@ -473,24 +473,26 @@ __device__ __forceinline__ void gateup_compute(const GateUpRegs<NJ>& g, const ui
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane >> 4, c = lane & 15;
   const int NB = H / 32;
+  // each activation block is read from LDS once and used for both row steps
+  float accs[2] = {0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int b = c + 16 * j;
+    if (b < NB) {
+      uint32_t xp[16];
+      const uint4* src = reinterpret_cast<const uint4*>(xs32 + b * 20);   // LayMX: 80-byte blocks
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 t = src[q];
+        xp[4 * q] = t.x; xp[4 * q + 1] = t.y; xp[4 * q + 2] = t.z; xp[4 * q + 3] = t.w;
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st) accs[st] = fmaf(mx_block_dot(g.cw[st][j], xp), e8m0_to_f32(g.sb[st][j]), accs[st]);
+    }
+  }
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
-    float acc = 0.f;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int b = c + 16 * j;
-      if (b < NB) {
-        uint32_t xp[16];
-        const uint4* src = reinterpret_cast<const uint4*>(xs32 + b * 20);   // LayMX: 80-byte blocks
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint4 t = src[q];
-          xp[4 * q] = t.x; xp[4 * q + 1] = t.y; xp[4 * q + 2] = t.z; xp[4 * q + 3] = t.w;
-        }
-        acc = fmaf(mx_block_dot(g.cw[st][j], xp), e8m0_to_f32(g.sb[st][j]), acc);
-      }
-    }
-    const float sum = sum16(acc);
+    const float sum = sum16(accs[st]);
     const float up = __shfl_xor(sum, 32);
     const int ri = i0 + 4 * wave + 2 * st + (r & 1);
     // lanes c < kCopiesA of the two gate rows each publish copy c: one store

@@ -813,6 +813,128 @@ __global__ void __launch_bounds__(256) router_topk_kernel(
   for (int e = threadIdx.x; e < n * T; e += 256) slot_w[e] = sw_tab[e];
 }
 
+// ---------------------------------------------------------------- router for 5..16 tokens
+
+// The router of a small batch or a longer draft (5 <= T <= WSX_MAX_T_MOE
+// tokens; [saipien] "Draft three tokens, verify four" for the verify pass
+// this generalizes).  The GEMV is the one above with the tokens staged in LDS
+// four at a time (their rows stay in registers across the chunks), so the
+// stage never exceeds 4 K bf16.  The last workgroup ranks each token on one
+// wavefront (wavefront w takes tokens w, w + 4, ...), then builds the compact
+// list from the T k selections with the whole workgroup: selection j keeps
+// its id if no earlier selection has it, and every selection's slot is the
+// number of distinct smaller ids.
+constexpr int kRouteChunk = 4;
+
+template <int WT, int RGPL, int P>
+__global__ void __launch_bounds__(256) router_topk_grouped_kernel(
+    const uint8_t* __restrict__ W, int E, int K, int k, const uint16_t* __restrict__ x, int T, float* logits,
+    int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, int32_t* __restrict__ expert_list,
+    float* __restrict__ slot_w, unsigned* counter) {
+  constexpr int DW = WTraits<WT>::EPG / 2;
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [kRouteChunk][K]
+  __shared__ int flag;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int G = K / WTraits<WT>::EPG;
+  const size_t row_bytes = (size_t)K * WTraits<WT>::ESZ;
+  const uint32_t* xs32 = reinterpret_cast<const uint32_t*>(xs);
+  for (int r0 = blockIdx.x * 4; r0 < E; r0 += gridDim.x * 4) {   // uniform across the workgroup
+    const int row = r0 + wave;
+    const bool ok = row < E;
+    uint4 wv[RGPL];
+#pragma unroll
+    for (int j = 0; j < RGPL; ++j) {
+      const int g = lane + 64 * j;
+      wv[j] = (ok && g < G) ? ld16(W + (size_t)row * row_bytes + (size_t)g * 16) : make_uint4(0, 0, 0, 0);
+    }
+    for (int tc = 0; tc < T; tc += kRouteChunk) {
+      const int nt = T - tc < kRouteChunk ? T - tc : kRouteChunk;
+      __syncthreads();   // the previous chunk's reads are done
+      const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)tc * K);
+      uint4* dst = reinterpret_cast<uint4*>(xs);
+      for (int c = threadIdx.x; c < nt * K / 8; c += 256) dst[c] = src[c];
+      __syncthreads();
+      if (ok) {
+        for (int t = 0; t < nt; ++t) {
+          float acc = 0.f;
+#pragma unroll
+          for (int j = 0; j < RGPL; ++j) {
+            const int g = lane + 64 * j;
+            if (g < G) {
+              uint32_t xp[DW];
+#pragma unroll
+              for (int d = 0; d < DW; ++d) xp[d] = xs32[(size_t)t * (K / 2) + (size_t)g * DW + d];
+              acc += granule_dot<WT>(wv[j], xp);
+            }
+          }
+          const float sres = wave_sum_dpp(acc);
+          if (lane == 0) st_dev(logits + (size_t)(tc + t) * E + row, sres);
+        }
+      }
+    }
+  }
+  if (!last_block_arrived(counter, gridDim.x, &flag)) return;
+
+  // ---- last workgroup: per token, top-k and softmax in rank order
+  __shared__ RankKey wcand[4][8 * 4 * P];
+  __shared__ float wrv[4][WSX_MAX_K];
+  __shared__ int wrid[4][WSX_MAX_K];
+  __shared__ int sel_id[WSX_MAX_T_MOE * WSX_MAX_K];
+  __shared__ float sel_w[WSX_MAX_T_MOE * WSX_MAX_K];
+  __shared__ int first[WSX_MAX_T_MOE * WSX_MAX_K];
+  __shared__ float sw_tab[WSX_MAX_T_MOE * WSX_MAX_K * WSX_MAX_T_MOE];
+  for (int t = wave; t < T; t += 4) {
+    wave_topk<4 * P>(logits + (size_t)t * E, E, k, wcand[wave], wrv[wave], wrid[wave]);
+    if (lane < k) {
+      const float top = wrv[wave][0];
+      float zs = 0.f, mine = 0.f;
+#pragma unroll
+      for (int j = 0; j < WSX_MAX_K; ++j) {
+        if (j < k) {
+          const float z = __expf(wrv[wave][j] - top);
+          zs += z;
+          if (j == lane) mine = z;
+        }
+      }
+      const float wj = mine / zs;
+      const int id = wrid[wave][lane];
+      topk_ids[t * k + lane] = id;
+      topk_w[t * k + lane] = wj;
+      sel_id[t * k + lane] = id;
+      sel_w[t * k + lane] = wj;
+    }
+    // the next token reuses this wavefront's scratch: only the compiler has
+    // to keep the order (LDS accesses of one wavefront complete in order)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  const int n = T * k;
+  for (int e = threadIdx.x; e < n * T; e += 256) sw_tab[e] = 0.f;
+  __syncthreads();
+  for (int j = threadIdx.x; j < n; j += 256) {
+    const int id = sel_id[j];
+    int f = 1;
+    for (int i = 0; i < j; ++i) f &= (sel_id[i] != id);
+    first[j] = f;
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < n; j += 256) {
+    const int id = sel_id[j];
+    int rank = 0;
+    for (int i = 0; i < n; ++i) rank += first[i] & (sel_id[i] < id);
+    if (first[j]) expert_list[1 + rank] = id;
+    sw_tab[rank * T + j / k] = sel_w[j];   // a token's k ids are distinct: one entry per (slot, token)
+  }
+  if (threadIdx.x == 0) {
+    int tot = 0;
+    for (int i = 0; i < n; ++i) tot += first[i];
+    expert_list[0] = tot;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < n * T; e += 256) slot_w[e] = sw_tab[e];
+}
+
 // ---------------------------------------------------------------- launchers
 
 template <int WT, int T>
@@ -949,9 +1071,42 @@ bool router_shape_supported(int router_dtype, int K) {
   return rgpl == 1 || rgpl == 2 || rgpl == 4 || rgpl == 5 || rgpl == 8 || rgpl == 10 || rgpl == 16 || rgpl == 32;
 }
 
+template <int WT>
+static hipError_t launch_router_grouped(const void* W, int E, int K, int k, const uint16_t* x, int T, float* logits,
+                                        int32_t* ids, float* w, int32_t* el, float* sw, unsigned* counter,
+                                        hipStream_t st) {
+  const int G = K / WTraits<WT>::EPG;
+  const int rgpl = (G + 63) / 64;
+  const int grid = (E + 3) / 4;
+  const size_t lds = (size_t)kRouteChunk * K * 2;
+  const bool small = E <= 512;
+#define WSX_RG_CASE(N)                                                                                            \
+  case N:                                                                                                         \
+    if (small)                                                                                                    \
+      router_topk_grouped_kernel<WT, N, 2><<<grid, 256, lds, st>>>((const uint8_t*)W, E, K, k, x, T, logits, ids, \
+                                                                   w, el, sw, counter);                           \
+    else                                                                                                          \
+      router_topk_grouped_kernel<WT, N, 4><<<grid, 256, lds, st>>>((const uint8_t*)W, E, K, k, x, T, logits, ids, \
+                                                                   w, el, sw, counter);                           \
+    break;
+  switch (rgpl) {
+    WSX_RG_CASE(1) WSX_RG_CASE(2) WSX_RG_CASE(4) WSX_RG_CASE(5) WSX_RG_CASE(8) WSX_RG_CASE(10) WSX_RG_CASE(16)
+    WSX_RG_CASE(32)
+    default: return hipErrorInvalidValue;
+  }
+#undef WSX_RG_CASE
+  return hipGetLastError();
+}
+
 hipError_t launch_router(int router_dtype, const void* W, int E, int K, int k, const uint16_t* x, int T, int norm,
                          uint16_t* u_out, float* logits, int32_t* ids, float* w, int32_t* el, float* sw,
                          unsigned* counter, hipStream_t st) {
+  if (T > WSX_MAX_T) {
+    if (norm) return hipErrorInvalidValue;   // the normalized (decode-step) router takes at most WSX_MAX_T tokens
+    return router_dtype == WSX_DTYPE_F32
+               ? launch_router_grouped<W_F32>(W, E, K, k, x, T, logits, ids, w, el, sw, counter, st)
+               : launch_router_grouped<W_BF16>(W, E, K, k, x, T, logits, ids, w, el, sw, counter, st);
+  }
 #define WSX_T_CASE(DT, WTV, TV) \
   if (router_dtype == DT && T == TV) return launch_router_t<WTV, TV>(W, E, K, k, x, norm, u_out, logits, ids, w, el, sw, counter, st);
   WSX_T_CASE(WSX_DTYPE_BF16, W_BF16, 1) WSX_T_CASE(WSX_DTYPE_BF16, W_BF16, 2)

@@ -163,19 +163,6 @@ __global__ void __launch_bounds__(256) moe_gateup_kernel(const uint16_t* __restr
 // activations from LDS.  Products are exact; the fp32 sums differ from a
 // sequential order only by rounding.  The four quarter sums are added in
 // wavefront order.
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(4))) float f32x4_t;
-
-__device__ __forceinline__ bf16x8_t fp4x8_to_bf16x8(uint32_t w, float scale) {
-  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
-  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
-  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
-  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
-  bf16x8_t r;
-  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-  return r;
-}
 
 template <int T, int NQ>   // NQ: groups of 4 MX blocks per wavefront quarter of K
 __global__ void __launch_bounds__(256) moe_gateup_mfma_kernel(const uint16_t* __restrict__ x, int H, int I, int E,
@@ -247,6 +234,82 @@ __global__ void __launch_bounds__(256) moe_gateup_mfma_kernel(const uint16_t* __
   }
   __syncthreads();
   if (threadIdx.x < 16 * T) {
+    const int rr = threadIdx.x % 16, t = threadIdx.x / 16;
+    const float g = ((red[0][0][rr][t] + red[1][0][rr][t]) + red[2][0][rr][t]) + red[3][0][rr][t];
+    const float u = ((red[0][1][rr][t] + red[1][1][rr][t]) + red[2][1][rr][t]) + red[3][1][rr][t];
+    a_out[((size_t)slot * T + t) * I + i0 + rr] = silu(g) * u;
+  }
+}
+
+// Gate/up + SwiGLU for 5..16 tokens (a small batch or a longer draft), on the
+// matrix cores as above with the tokens as the MFMA's columns; the token
+// columns take their activations straight from global memory (the T rows are
+// read by every workgroup and stay in the caches), so no LDS stage limits T.
+template <int NQ>
+__global__ void __launch_bounds__(256) moe_gateup_mfma_g_kernel(const uint16_t* __restrict__ x, int T, int H, int I,
+                                                                int E, int max_slots, const uint8_t* __restrict__ w13c,
+                                                                const uint8_t* __restrict__ w13s,
+                                                                const uint8_t* __restrict__ sh13c,
+                                                                const uint8_t* __restrict__ sh13s,
+                                                                const int32_t* __restrict__ expert_list,
+                                                                float* __restrict__ a_out) {
+  const int slot = blockIdx.y;
+  int n_active = expert_list[0];
+  n_active = n_active < 0 ? 0 : (n_active > max_slots - 1 ? max_slots - 1 : n_active);
+  const bool has_sh = sh13c != nullptr;
+  const int i0 = blockIdx.x * 16;
+  const uint8_t *C, *S;
+  if (!slot_expert(slot, n_active, has_sh, E, expert_list, w13c, w13s, sh13c, sh13s, (size_t)2 * I * (H / 2),
+                   (size_t)2 * I * (H / 32), &C, &S)) {
+    if (slot < n_active + (has_sh ? 1 : 0))
+      for (int i = threadIdx.x; i < 16 * T; i += 256) a_out[((size_t)slot * T + i / 16) * I + i0 + (i % 16)] = 0.f;
+    return;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = lane & 15, q = lane >> 4;
+  const int NB = H / 32;
+  const int b0 = wave * 4 * NQ;
+  const size_t rowc = H / 2, rows = H / 32;
+  uint4 cw[2][NQ];
+  float sc[2][NQ];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = h * I + i0 + row;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const int b = b0 + 4 * j + q;
+      const bool ok = b < NB;
+      cw[h][j] = ok ? ld16(C + r * rowc + (size_t)b * 16) : make_uint4(0, 0, 0, 0);
+      sc[h][j] = ok ? e8m0_to_f32(S[r * rows + b]) : 0.f;
+    }
+  }
+  __shared__ float red[4][2][16][WSX_MAX_T_MOE];
+  f32x4_t dg = {0.f, 0.f, 0.f, 0.f}, du = {0.f, 0.f, 0.f, 0.f};
+  const int col = row;   // B operand: lane (col, q), token col
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const int b = b0 + 4 * j + q;
+    const bool ok = b < NB;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      uint4 xv = make_uint4(0, 0, 0, 0);
+      if (col < T && ok) xv = ld16(x + (size_t)col * H + b * 32 + m * 8);
+      const bf16x8_t bx = __builtin_bit_cast(bf16x8_t, xv);
+      const uint32_t wg = m == 0 ? cw[0][j].x : m == 1 ? cw[0][j].y : m == 2 ? cw[0][j].z : cw[0][j].w;
+      const uint32_t wu = m == 0 ? cw[1][j].x : m == 1 ? cw[1][j].y : m == 2 ? cw[1][j].z : cw[1][j].w;
+      dg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4x8_to_bf16x8(wg, sc[0][j]), bx, dg, 0, 0, 0);
+      du = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4x8_to_bf16x8(wu, sc[1][j]), bx, du, 0, 0, 0);
+    }
+  }
+  if (col < T) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      red[wave][0][4 * q + r][col] = dg[r];
+      red[wave][1][4 * q + r][col] = du[r];
+    }
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < 16 * T) {
     const int rr = threadIdx.x % 16, t = threadIdx.x / 16;
     const float g = ((red[0][0][rr][t] + red[1][0][rr][t]) + red[2][0][rr][t]) + red[3][0][rr][t];
     const float u = ((red[0][1][rr][t] + red[1][1][rr][t]) + red[2][1][rr][t]) + red[3][1][rr][t];
@@ -491,6 +554,159 @@ __global__ void __launch_bounds__(256) moe_down_grouped_kernel(
   }
 }
 
+// Down + weighted combine + residual for 5..16 tokens, over expert-sorted
+// token lists: the slots are the active experts in ascending id order, and
+// slot s's tokens are those with a nonzero weight slot_w[s][t] (all tokens for
+// the shared expert).  Workgroup (tile, g) owns rows n0 .. n0+31 and the
+// slots 4g .. 4g+3, one per wavefront, as in the grouped kernel above; a
+// wavefront takes its slot's tokens four at a time, staging their activations
+// in LDS and forming the 32 rows x 4 tokens of partial sums from the same
+// decoded weights, so the work follows the routed (slot, token) pairs, not
+// slots x T.  Each slot's weighted contribution per (token, row) lands in LDS,
+// the four wavefronts are added in slot order, and the groups are added in
+// group order by the tile's last workgroup.
+template <int NKB>
+__global__ void __launch_bounds__(256) moe_down_sparse_kernel(
+    int T, int H, int I, int E, int max_slots, const uint8_t* __restrict__ w2c, const uint8_t* __restrict__ w2s,
+    const uint8_t* __restrict__ sh2c, const uint8_t* __restrict__ sh2s, const int32_t* __restrict__ expert_list,
+    const float* __restrict__ slot_w, const float* __restrict__ a_in, const uint16_t* __restrict__ residual,
+    float* __restrict__ out_y, uint16_t* __restrict__ out_h, uint16_t* __restrict__ out_h2, float* part,
+    unsigned* counters) {
+  constexpr int TC = 4;   // tokens per pass
+  int n_active = expert_list[0];
+  n_active = n_active < 0 ? 0 : (n_active > max_slots - 1 ? max_slots - 1 : n_active);
+  const bool has_sh = sh2c != nullptr;
+  const int nslots = n_active + (has_sh ? 1 : 0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kg = lane & 7, rq = lane >> 3;
+  const int n0 = blockIdx.x * kDnRows;
+  const int g = blockIdx.y, s = 4 * g + wave;
+  const int NB = I / 32;
+  const int lstride = NB * 36;   // floats per token row in LDS
+  extern __shared__ __attribute__((aligned(16))) float as[];   // [4][TC][lstride]
+  __shared__ float yw[4][WSX_MAX_T_MOE][kDnRows];
+  __shared__ int flag;
+  float* aw = as + (size_t)wave * TC * lstride;
+  for (int i = lane; i < WSX_MAX_T_MOE * kDnRows; i += 64) yw[wave][i / kDnRows][i % kDnRows] = 0.f;
+  const uint8_t *C = nullptr, *S = nullptr;
+  const bool active = s < nslots && slot_expert(s, n_active, has_sh, E, expert_list, w2c, w2s, sh2c, sh2s,
+                                                (size_t)H * (I / 2), (size_t)H * (I / 32), &C, &S);
+  if (active) {
+    const size_t rowc = I / 2, rows = I / 32;
+    uint4 cw[NKB][4];
+    float sc[NKB][4];
+#pragma unroll
+    for (int b = 0; b < NKB; ++b) {
+      const int kb = kg + 8 * b;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = n0 + 4 * rq + r;
+        cw[b][r] = kb < NB ? ld16(C + row * rowc + (size_t)kb * 16) : make_uint4(0, 0, 0, 0);
+        sc[b][r] = kb < NB ? e8m0_to_f32(S[row * rows + kb]) : 0.f;
+      }
+    }
+    // the slot's token list: lane t < T holds token t's weight
+    const float wl = lane < T ? (s < n_active ? slot_w[s * T + lane] : 1.0f) : 0.f;
+    unsigned long long tm = __ballot(lane < T && wl != 0.f);
+    while (tm) {
+      int tok[TC];
+      float wt[TC];
+#pragma unroll
+      for (int j = 0; j < TC; ++j) {
+        tok[j] = tm ? (int)__builtin_ctzll(tm) : -1;
+        wt[j] = tok[j] >= 0 ? readlane_f(wl, tok[j]) : 0.f;
+        tm &= tm - 1;
+      }
+      // these tokens' activations -> LDS (32-value blocks at a 36-float stride)
+      const int nq = I / 4;
+#pragma unroll
+      for (int j = 0; j < TC; ++j) {
+        if (tok[j] < 0) continue;
+        const float4* src = reinterpret_cast<const float4*>(a_in + ((size_t)s * T + tok[j]) * I);
+        for (int q4 = lane; q4 < nq; q4 += 64)
+          *reinterpret_cast<float4*>(aw + j * lstride + dpos(4 * q4)) = src[q4];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      float acc[4][TC];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < TC; ++j) acc[r][j] = 0.f;
+#pragma unroll
+      for (int b = 0; b < NKB; ++b) {
+        const int kb = kg + 8 * b;
+        if (kb >= NB) continue;
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          float av[TC][8];
+#pragma unroll
+          for (int j = 0; j < TC; ++j) {
+            const float4* ap = reinterpret_cast<const float4*>(aw + j * lstride + kb * 36 + c4 * 8);
+            const float4 v0 = ap[0], v1 = ap[1];
+            av[j][0] = v0.x; av[j][1] = v0.y; av[j][2] = v0.z; av[j][3] = v0.w;
+            av[j][4] = v1.x; av[j][5] = v1.y; av[j][6] = v1.z; av[j][7] = v1.w;
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t wd = c4 == 0 ? cw[b][r].x : c4 == 1 ? cw[b][r].y : c4 == 2 ? cw[b][r].z : cw[b][r].w;
+            const f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc[b][r], 0);
+            const f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc[b][r], 1);
+            const f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc[b][r], 2);
+            const f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc[b][r], 3);
+#pragma unroll
+            for (int j = 0; j < TC; ++j) {
+              float v = acc[r][j];
+              v = fmaf(p0.x, av[j][0], v);
+              v = fmaf(p0.y, av[j][1], v);
+              v = fmaf(p1.x, av[j][2], v);
+              v = fmaf(p1.y, av[j][3], v);
+              v = fmaf(p2.x, av[j][4], v);
+              v = fmaf(p2.y, av[j][5], v);
+              v = fmaf(p3.x, av[j][6], v);
+              v = fmaf(p3.y, av[j][7], v);
+              acc[r][j] = v;
+            }
+          }
+        }
+      }
+      // weighted row sums (fixed DPP tree over the 8 lanes of a row group);
+      // each (token, row) of this slot is written by one lane
+#pragma unroll
+      for (int j = 0; j < TC; ++j) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = sum8(acc[r][j] * wt[j]);
+          if (kg == 0 && tok[j] >= 0) yw[wave][tok[j]][4 * rq + r] = v;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < T * kDnRows; i += 256) {
+    const int t = i / kDnRows, rr = i % kDnRows;
+    const float v = ((yw[0][t][rr] + yw[1][t][rr]) + yw[2][t][rr]) + yw[3][t][rr];
+    st_dev(part + ((size_t)g * T + t) * H + n0 + rr, v);
+  }
+  if (!last_block_arrived(counters + blockIdx.x * 16, gridDim.y, &flag)) return;
+  for (int i = threadIdx.x; i < T * kDnRows; i += 256) {
+    const int t = i / kDnRows, rr = i % kDnRows;
+    float y = 0.f;
+    for (int gg = 0; gg < (int)gridDim.y; ++gg) y += ld_dev(part + ((size_t)gg * T + t) * H + n0 + rr);
+    const size_t o = (size_t)t * H + n0 + rr;
+    if (out_y) out_y[o] = y;
+    if (residual) {
+      const uint16_t h = f32_to_bf16_rne(bf16_bits_to_f32(residual[o]) + y);
+      if (out_h) out_h[o] = h;
+      if (out_h2) out_h2[o] = h;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 
 bool experts_shape_supported(int H, int I) {
@@ -539,10 +755,28 @@ static hipError_t launch_gateup_mfma_t(const uint16_t* x, int H, int I, int E, i
   return hipGetLastError();
 }
 
+static hipError_t launch_gateup_g(const uint16_t* x, int T, int H, int I, int E, int max_slots, const uint8_t* w13c,
+                                  const uint8_t* w13s, const uint8_t* sh13c, const uint8_t* sh13s, const int32_t* el,
+                                  float* a, hipStream_t st) {
+  const int nq = (H / 32 + 15) / 16;
+  dim3 grid(I / 16, max_slots);
+#define WSX_GG_CASE(N)                                                                                        \
+  case N:                                                                                                     \
+    moe_gateup_mfma_g_kernel<N><<<grid, 256, 0, st>>>(x, T, H, I, E, max_slots, w13c, w13s, sh13c, sh13s, el, a); \
+    break;
+  switch (nq) {
+    WSX_GG_CASE(1) WSX_GG_CASE(2) WSX_GG_CASE(4) WSX_GG_CASE(5) WSX_GG_CASE(8) WSX_GG_CASE(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef WSX_GG_CASE
+  return hipGetLastError();
+}
+
 hipError_t launch_gateup(const uint16_t* x, int T, int H, int I, int E, int k, const uint8_t* w13c,
                          const uint8_t* w13s, const uint8_t* sh13c, const uint8_t* sh13s, const int32_t* el,
                          float* a, hipStream_t st) {
   const int max_slots = T * k + 1;
+  if (T > WSX_MAX_T) return launch_gateup_g(x, T, H, I, E, max_slots, w13c, w13s, sh13c, sh13s, el, a, st);
   if (T >= 2) {
     switch (T) {
       case 2: return launch_gateup_mfma_t<2>(x, H, I, E, max_slots, w13c, w13s, sh13c, sh13s, el, a, st);
@@ -608,11 +842,35 @@ static hipError_t launch_down_grouped_t(int H, int I, int E, int max_slots, cons
   return hipGetLastError();
 }
 
+static hipError_t launch_down_sparse(int T, int H, int I, int E, int max_slots, const uint8_t* w2c, const uint8_t* w2s,
+                                     const uint8_t* sh2c, const uint8_t* sh2s, const int32_t* el, const float* sw,
+                                     const float* a, const uint16_t* res, float* y, uint16_t* h, uint16_t* h2,
+                                     float* part, unsigned* counters, hipStream_t st) {
+  const int nkb = (I / 32 + 7) / 8;
+  dim3 grid(H / kDnRows, down_groups(max_slots));
+  const size_t lds = down_grouped_lds(4, I);
+#define WSX_DS_CASE(N)                                                                                          \
+  case N:                                                                                                       \
+    moe_down_sparse_kernel<N><<<grid, 256, lds, st>>>(T, H, I, E, max_slots, w2c, w2s, sh2c, sh2s, el, sw, a,  \
+                                                      res, y, h, h2, part, counters);                           \
+    break;
+  switch (nkb) {
+    WSX_DS_CASE(1) WSX_DS_CASE(2) WSX_DS_CASE(3) WSX_DS_CASE(4)
+    default: return hipErrorInvalidValue;
+  }
+#undef WSX_DS_CASE
+  return hipGetLastError();
+}
+
 hipError_t launch_down(int T, int H, int I, int E, int k, const uint8_t* w2c, const uint8_t* w2s,
                        const uint8_t* sh2c, const uint8_t* sh2s, const int32_t* el, const float* sw, const float* a,
                        const uint16_t* res, float* y, uint16_t* h, uint16_t* h2, float* part, unsigned* counters,
                        hipStream_t st) {
   const int max_slots = T * k + 1;
+  if (T > WSX_MAX_T) {
+    if (!part || !counters || !down_grouped_ok(4, H, I)) return hipErrorInvalidValue;
+    return launch_down_sparse(T, H, I, E, max_slots, w2c, w2s, sh2c, sh2s, el, sw, a, res, y, h, h2, part, counters, st);
+  }
   if (part && counters && down_grouped_ok(T, H, I)) {
     switch (T) {
       case 2: return launch_down_grouped_t<2>(H, I, E, max_slots, w2c, w2s, sh2c, sh2s, el, sw, a, res, y, h, h2, part, counters, st);

@@ -49,6 +49,20 @@ __device__ __forceinline__ bf16x2_t fp8x2_to_bf16x2(uint32_t w) {
 
 __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2_t, w); }
 
+// Eight E2M1 codes (one dword, element 2j in the low nibble of byte j) times
+// their power-of-two block scale -> eight bf16, exact (the matrix cores' A
+// operand for 8 consecutive elements).
+__device__ __forceinline__ bf16x8_t fp4x8_to_bf16x8(uint32_t w, float scale) {
+  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+  bf16x8_t r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
 __device__ __forceinline__ float dot2(bf16x2_t a, bf16x2_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
 }
