@@ -327,6 +327,20 @@ wsx_status moe_decode_step(const uint16_t* h_in, int T, const wsx_moe_stack* sta
                            void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * wsx_decode_step_path — how moe_decode_step runs a stack of this shape:
+ *   0  per-phase launches (T > 1, no shared expert, or a shape outside the
+ *      one-launch kernel's layout: E > 512, H > 4096, I > 2048, ...);
+ *   1  one launch, compiled ahead of time (H 2560 / I 768 / bf16 router, and
+ *      H 256 / I 64 / fp32 router);
+ *   2  one launch, compiled at run time with hipRTC on the first call for the
+ *      shape on each device (about a second), then reused.
+ * [saipien] "Kernels built for the shape you actually have": the pages' MoE
+ * kernels are specialized to the model's shapes at run time.  A failed
+ * run-time compilation makes moe_decode_step return WSX_ERR_HIP.
+ */
+int wsx_decode_step_path(int T, int router_dtype, int has_shared, int H, int I, int E, int k);
+
+/*
  * wsx_read_probe — measurement utility, not a step of the decode path: one
  * plain streaming read of `bytes` bytes at `buf` (16-byte loads, all issued
  * before use), the reference rate for "how fast can weights come out of

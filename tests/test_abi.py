@@ -185,3 +185,19 @@ def test_w4a8_argument_errors():
     assert f(*args(T=17)) == 4
     assert f(*args(act=MIS)) == 3
     assert f(*args(wsb=100)) == 5
+
+
+def test_decode_step_path_query():
+    """Which path a stack shape takes: the two shapes compiled ahead of time,
+    run-time compiled shapes inside the one-launch layout, per-phase otherwise."""
+    q = _lib.load().wsx_decode_step_path
+    assert q(1, 0, 1, 2560, 768, 512, 8) == 1            # Ling shape, bf16 router
+    assert q(1, 1, 1, 256, 64, 16, 2) == 1               # tiny shape, fp32 router
+    assert q(1, 0, 1, 512, 128, 64, 4) == 2              # compiled at run time
+    assert q(1, 1, 1, 384, 96, 40, 3) == 2
+    assert q(1, 0, 1, 256, 64, 16, 2) == 2               # the tiny shape with a bf16 router
+    assert q(4, 0, 1, 2560, 768, 512, 8) == 0            # several tokens: per-phase
+    assert q(1, 0, 0, 2560, 768, 512, 8) == 0            # no shared expert
+    assert q(1, 0, 1, 2560, 768, 1024, 8) == 0           # more experts than one routing workgroup ranks
+    assert q(1, 0, 1, 8192, 768, 512, 8) == 0            # beyond the kernel's register arrays
+    assert q(1, 7, 1, 2560, 768, 512, 8) == 0

@@ -57,6 +57,7 @@ _PROTOS = {
     "moe_decode_step_noalloc": [c_void_p, c_int, ctypes.POINTER(MoeStack), c_void_p, c_void_p, c_int,
                                 c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
     "wsx_read_probe": [c_void_p, c_size_t, c_void_p, c_void_p],
+    "wsx_decode_step_path": [c_int, c_int, c_int, c_int, c_int, c_int, c_int],
     "wsx_moe_workspace_bytes": [c_int, c_int, c_int, c_int, c_int],
     "wsx_lm_head_workspace_bytes": [c_int, c_int, c_int],
     "wsx_decode_step_workspace_bytes": [c_int, c_int, c_int, c_int, c_int, c_int],
@@ -68,7 +69,7 @@ _PROTOS = {
 _RESTYPES = {"wsx_moe_workspace_bytes": c_size_t, "wsx_lm_head_workspace_bytes": c_size_t,
              "wsx_decode_step_workspace_bytes": c_size_t, "wsx_sample_workspace_bytes": c_size_t,
              "wsx_lm_head_sample_workspace_bytes": c_size_t, "wsx_status_string": c_char_p,
-             "wsx_build_info": c_char_p}
+             "wsx_build_info": c_char_p, "wsx_decode_step_path": c_int}
 EXPORTS = tuple(_PROTOS)
 
 _lib = None

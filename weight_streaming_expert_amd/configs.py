@@ -51,6 +51,11 @@ LM_HEAD = Workload("lm_head_157184x2560_fp8", T=1, V=157184, moe=MoEShape(H=2560
 VERIFY = Workload("mtp_verify_t4", T=4, moe=LING_MOE, layers=1, V=157184, steps=100, seed=41)
 # A small batch or a longer draft: the MoE layer on 16 tokens with independent top-8 routing.
 GROUPED16 = Workload("moe_layer_grouped_t16", T=16, moe=LING_MOE, layers=1, steps=20, seed=61)
+# Stacks of shapes the one-launch step is not compiled for ahead of time (compiled at run time).
+RTC_A = Workload("rtc_stack_h512_e64_top4_i128", T=1, layers=2, V=2048, seed=71,
+                 moe=MoEShape(H=512, I=128, E=64, k=4, router_dtype="bf16"))
+RTC_B = Workload("rtc_stack_h384_e40_top3_i96", T=1, layers=3, V=1000, seed=72,
+                 moe=MoEShape(H=384, I=96, E=40, k=3, router_dtype="f32", scale_dist=("uniform", -4, 2)))
 # Full decode step: 32 stacked MoE layers (512 experts each) then the FP8 head, 2000 seeded tokens.
 DECODE_STEP = Workload("decode_step_32x_moe_fp8_head", T=1, moe=LING_MOE, layers=32, V=157184, steps=2000, seed=51)
 

@@ -422,6 +422,11 @@ wsx_status moe_decode_step(const uint16_t* h_in, int T, const wsx_moe_stack* sk,
                                    base + W.head, s));
 }
 
+int wsx_decode_step_path(int T, int router_dtype, int has_shared, int H, int I, int E, int k) {
+  if (router_dtype != WSX_DTYPE_BF16 && router_dtype != WSX_DTYPE_F32) return 0;
+  return fused_step_path(T, router_dtype, has_shared != 0, H, I, E, k);
+}
+
 wsx_status wsx_read_probe(const void* buf, size_t bytes, uint32_t* out, void* stream) {
   if (!buf || !out) return WSX_ERR_NULL;
   if (bytes == 0 || bytes % 16) return WSX_ERR_SHAPE;
@@ -447,7 +452,7 @@ const char* wsx_status_string(wsx_status s) {
 #define WSX_STR(x) WSX_STR2(x)
 const char* wsx_build_info(void) {
   return "libwsx arch=gfx950 hip=" WSX_STR(HIP_VERSION_MAJOR) "." WSX_STR(HIP_VERSION_MINOR)
-         " kernels=decode_step<T1;one-launch>,router_topk<bf16|f32,T1-4;rank-count>,"
+         " kernels=decode_step<T1;one-launch;aot:Ling-bf16,tiny-f32;hiprtc:other-shapes>,router_topk<bf16|f32,T1-4;rank-count>,"
          "moe_gateup<T1;valu-dot2|T2-4;mfma-bf16>,moe_down<T1;valu|T2-4;grouped>,"
          "lm_head<fp8|bf16,T1;wide-per-CU>,lm_head<fp8,T2-4;mfma-bf16>,lm_head<bf16,T2-4>,quant_fp8,sample<topk<=64,topp>";
 }

@@ -51,6 +51,8 @@ hipError_t launch_w4a8_experts(const uint16_t* x, int T, int H, int I, int E, in
 
 // decode_step.hip: the whole 1-token decode step in one launch
 bool fused_step_supported(int T, int router_dtype, bool has_shared, int H, int I, int E, int k);
+// 0: per-phase launches, 1: one launch compiled ahead of time, 2: one launch compiled at run time (hipRTC)
+int fused_step_path(int T, int router_dtype, bool has_shared, int H, int I, int E, int k);
 size_t fused_step_workspace_bytes(int H, int I, int E, int k, int V);
 hipError_t launch_fused_step(const wsx_moe_stack* sk, const uint16_t* h_in, const uint8_t* hq, const float* hs, int V,
                              uint16_t* h_out, float* logits, int32_t* argmax, uint16_t* h_trace, uint16_t* u_trace,

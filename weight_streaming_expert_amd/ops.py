@@ -62,6 +62,14 @@ def decode_step_workspace_bytes(T, H, I, E, k, V):
     return int(_lib.load().wsx_decode_step_workspace_bytes(T, H, I, E, k, V))
 
 
+def decode_step_path(T, stack):
+    """0: per-phase launches, 1: one launch compiled ahead of time, 2: one launch
+    compiled at run time (hipRTC) for this stack's shape."""
+    dt = DTYPE_F32 if stack.w_router.dtype == torch.float32 else DTYPE_BF16
+    return int(_lib.load().wsx_decode_step_path(T, dt, int(stack.shared is not None), stack.H, stack.I, stack.E,
+                                                stack.k))
+
+
 def build_info():
     return _lib.load().wsx_build_info().decode()
 
