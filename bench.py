@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--head-reps", type=int, default=200)
     ap.add_argument("--kernel-reps", type=int, default=200)
+    ap.add_argument("--breakdown-reps", type=int, default=100,
+                    help="samples per breakdown row (at most the workload's seeded inputs); small values serve "
+                         "hardware-counter runs")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB device-to-device 3 times (a plain copy "
                          "kernel of known size, used to scale hardware byte counters)")
@@ -170,10 +173,11 @@ def main():
     # ------------------------------------------------------------------ dominant kernel: the one-launch step
     # Ten back-to-back steps per graph: the average launch duration of the
     # step kernel itself, measured with events on the launch stream.
+    am_k = torch.full((10,), -2, dtype=torch.int32, device=dev)
     gk = torch.cuda.CUDAGraph()
     with torch.cuda.graph(gk):
         for j in range(10):
-            step(W + j, j, am_eager)
+            step(W + j, j, am_k)
     gk.replay()
     torch.cuda.synchronize()
     reps = max(1, args.kernel_reps // 10)
@@ -243,7 +247,8 @@ def main():
     }
 
     if not args.no_breakdown:
-        result["breakdown"] = breakdown(torch, ops, configs, inputs, dev, stack, head, head_w, wl, quant_us, probe)
+        result["breakdown"] = breakdown(torch, ops, configs, inputs, dev, stack, head, head_w, wl, quant_us, probe,
+                                        reps=args.breakdown_reps)
     if not args.no_cpu:
         # the timed steps whose every layer is checked against the oracle: the
         # first, middle and last of the timed range (the last one's residual
@@ -297,7 +302,8 @@ def read_probe(torch, ops, dev, gib=1, reps=10):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_kernel_hbm_counters.md")
-STEP_SOURCES = ("weight_streaming_expert_amd/csrc/decode_step.hip", "weight_streaming_expert_amd/csrc/wsx_device.h")
+STEP_SOURCES = ("weight_streaming_expert_amd/csrc/decode_step_kernel.h", "weight_streaming_expert_amd/csrc/decode_step.hip",
+                "weight_streaming_expert_amd/csrc/wsx_device.h")
 
 
 def step_source_digest():
@@ -371,7 +377,7 @@ def _stats(ts, bytes_per_sample=None, probe=None):
     return d
 
 
-def breakdown(torch, ops, configs, inputs, dev, stack, head, head_w, wl, quant_us, probe):
+def breakdown(torch, ops, configs, inputs, dev, stack, head, head_w, wl, quant_us, probe, reps=100):
     m = wl.moe
     H, I, E, k, V = m.H, m.I, m.E, m.k, head.V
     flush_buf = torch.ones(1 << 27, dtype=torch.int64, device=dev)   # 1 GiB
@@ -398,7 +404,7 @@ def breakdown(torch, ops, configs, inputs, dev, stack, head, head_w, wl, quant_u
             (configs.GROUPED16, "moe_layer_w4a8_grouped_t16", ops.moe_expert_gemv_w4a8))
     for wlx, name, experts in rows:
         T = wlx.T
-        xs = [bf16_dev(inputs.activations(wlx, s)) for s in range(wlx.steps)]
+        xs = [bf16_dev(inputs.activations(wlx, s)) for s in range(min(wlx.steps, reps))]
         x = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         res = torch.empty_like(x)
         ws = ops.workspace(ops.moe_workspace_bytes(T, H, I, E, k), dev)
@@ -428,7 +434,7 @@ def breakdown(torch, ops, configs, inputs, dev, stack, head, head_w, wl, quant_u
         x = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         hws = ops.workspace(ops.lm_head_workspace_bytes(T, V, H), dev)
         rows = lambda i, T=T: torch.cat([xh[(i * T + j) % len(xh)] for j in range(T)])
-        ts = _timed_graph(torch, lambda: head.gemv_argmax(x, ws=hws), flush, reps=100,
+        ts = _timed_graph(torch, lambda: head.gemv_argmax(x, ws=hws), flush, reps=reps,
                           before=lambda i, x=x, rows=rows: x.copy_(rows(i)))
         out[f"lm_head_fp8_t{T}"] = _stats(ts, configs.head_bytes(V, H, T, True), probe)
     x = bf16_dev(inputs.normal_bf16((wl.seed, 8), (4, H), 1.0))
@@ -439,17 +445,17 @@ def breakdown(torch, ops, configs, inputs, dev, stack, head, head_w, wl, quant_u
         u = torch.from_numpy(inputs.uniform_f32((wl.seed, 9, T), (T,))).to(dev)
         logits_t, _ = head.gemv_argmax(xt)
         sws = ops.workspace(ops._lib.load().wsx_sample_workspace_bytes(T, V, 29), dev)
-        ts = _timed_graph(torch, lambda: ops.lm_sample_topk_topp(logits_t, 0.6, 29, 0.95, u, ws=sws), flush)
+        ts = _timed_graph(torch, lambda: ops.lm_sample_topk_topp(logits_t, 0.6, 29, 0.95, u, ws=sws), flush, reps=reps)
         t = _stats(ts)
         t.update(bytes=T * V * 4)
         out[f"sample_topk_topp_t{T}"] = t
         fws = ops.workspace(ops._lib.load().wsx_lm_head_sample_workspace_bytes(T, V, H, 29), dev)
         ts = _timed_graph(torch, lambda: ops.lm_head_gemv_fp8_sample(head.q, head.s, xt, 0.6, 29, 0.95, u, ws=fws),
-                          flush)
+                          flush, reps=reps)
         out[f"lm_head_fp8_sample_t{T}"] = _stats(ts, configs.head_bytes(V, H, T, True), probe)
     hws = ops.workspace(ops.lm_head_workspace_bytes(1, V, H), dev)
     x1 = torch.empty((1, H), dtype=torch.bfloat16, device=dev)
-    ts = _timed_graph(torch, lambda: ops.lm_head_gemv_bf16_argmax(head_w, x1, ws=hws), flush, reps=100,
+    ts = _timed_graph(torch, lambda: ops.lm_head_gemv_bf16_argmax(head_w, x1, ws=hws), flush, reps=reps,
                       before=lambda i: x1.copy_(xh[i % len(xh)]))
     out["lm_head_bf16_t1"] = _stats(ts, configs.head_bytes(V, H, 1, False), probe)
     out["bf16_over_fp8_time"] = round(out["lm_head_bf16_t1"]["median_us"] / out["lm_head_fp8_t1"]["median_us"], 3)
@@ -457,7 +463,7 @@ def breakdown(torch, ops, configs, inputs, dev, stack, head, head_w, wl, quant_u
     # the first call's time including the 403 MB output allocation
     qq, qsc = torch.empty_like(head.q), torch.empty_like(head.s)
     ts = _timed_graph(torch, lambda: ops._lib.call("lm_head_quantize_fp8", ops._p(head_w), V, H, ops._p(qq),
-                                                   ops._p(qsc), ops._stream(dev)), flush, reps=20)
+                                                   ops._p(qsc), ops._stream(dev)), flush, reps=min(20, reps))
     assert torch.equal(qq, head.q) and torch.equal(qsc, head.s)
     t = _stats(ts, V * H * 2 + V * H + V * 4, probe)
     t.update(first_call_incl_alloc_us=round(quant_us, 1))
