@@ -254,14 +254,25 @@ wsx_status lm_sample_topk_topp(const float* logits, int V, int T, float temperat
                                void* stream);
 
 /*
- * lm_head_gemv_fp8_sample — the FP8 head of lm_head_gemv_fp8_argmax followed
- * on the same stream by lm_sample_topk_topp on its logits: the sampling
- * decode of [ncij] "What happens on a real workload?" in place of greedy.
- * logits float [T][V] is required (the sampler reads it).  Limits: those of
- * both calls.  Workspace: wsx_lm_head_sample_workspace_bytes(T, V, K, top_k),
- * zero-filled before its first use.
+ * lm_head_gemv_fp8_sample — the FP8 head of lm_head_gemv_fp8_argmax with the
+ * sampler of lm_sample_topk_topp on its logits: the sampling decode of [ncij]
+ * "What happens on a real workload?" in place of greedy.  Results are those of
+ * lm_sample_topk_topp on the logits written here, bit for bit.  For T = 1 on
+ * the head shapes the wide kernel serves (wsx_lm_head_sample_path returns 1)
+ * it is one launch: each wavefront of the head publishes the maximum of the
+ * rows it streamed and the last workgroup to finish selects the top_k and
+ * draws; otherwise the head and the two sampler launches run in turn on the
+ * stream.  logits float [T][V] is required (an output in both forms).
+ * Limits: those of both calls.  A NaN logit is never drawn in the one-launch
+ * form; with fewer than top_k logits that are numbers the token is unspecified
+ * (-1 when none is).  Workspace: wsx_lm_head_sample_workspace_bytes(T, V, K,
+ * top_k), zero-filled before its first use; its counter returns to zero, so
+ * it is reusable without clearing; calls that share it must not overlap.
  */
 size_t wsx_lm_head_sample_workspace_bytes(int T, int V, int K, int top_k);
+/* 1: lm_head_gemv_fp8_sample runs as one launch on the current device for
+ * these sizes; 0: as three launches; -1: the sizes are not supported. */
+int wsx_lm_head_sample_path(int T, int V, int K, int top_k);
 wsx_status lm_head_gemv_fp8_sample(const uint8_t* q, const float* row_scale, int V, int K,
                                    const uint16_t* x, int T, float temperature, int top_k,
                                    float top_p, const float* uniforms, float* logits,

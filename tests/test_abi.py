@@ -144,6 +144,15 @@ def test_sample_argument_errors():
     assert lib.wsx_sample_workspace_bytes(1, 10, 11) == 0
     head_need = lib.wsx_lm_head_sample_workspace_bytes(4, 157184, 2560, 29)
     assert head_need == lib.wsx_lm_head_workspace_bytes(4, 157184, 2560) + 256 + 4 * 2456 * 30 * 8
+    # one row: room for the one-launch form's published maxima as well (up to 512 workgroups: 16 chunk
+    # maxima and the workgroup's maximum each)
+    head = lib.wsx_lm_head_workspace_bytes(1, 157184, 2560) + 256
+    assert lib.wsx_lm_head_sample_workspace_bytes(1, 157184, 2560, 29) == head + 2456 * 30 * 8
+    assert lib.wsx_lm_head_sample_workspace_bytes(1, 1000, 2560, 29) == head + 512 * 17 * 8
+    assert lib.wsx_lm_head_sample_path(2, 157184, 2560, 29) == 0
+    assert lib.wsx_lm_head_sample_path(5, 157184, 2560, 29) == -1
+    assert lib.wsx_lm_head_sample_path(1, 157184, 2560, 65) == -1
+    assert lib.wsx_lm_head_sample_path(1, 157184, 100, 29) == -1
     f = lib.lm_head_gemv_fp8_sample
     assert f(None, FAKE, 157184, 2560, FAKE, 1, 0.6, 29, 0.95, FAKE, FAKE, FAKE, None, None, FAKE, head_need, None) == 1
     assert f(FAKE, FAKE, 157184, 2560, FAKE, 1, 0.6, 29, 0.95, FAKE, None, FAKE, None, None, FAKE, head_need, None) == 1

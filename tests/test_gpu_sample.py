@@ -12,6 +12,7 @@ import pytest
 import torch
 
 from oracle import compare as C
+from oracle import formats as F
 from oracle import head as OH
 from oracle import sample as OS
 from weight_streaming_expert_amd import configs, inputs
@@ -178,3 +179,100 @@ def test_sampler_is_deterministic(ops):
         b = run_sampler(ops, z, 0.6, 29, 0.95, u)
         for x, y in zip(a, b):
             assert np.array_equal(x, y)
+
+
+# ---------------------------------------------------------------- the one-launch form (T = 1)
+
+def test_one_launch_path_is_taken(ops):
+    assert ops.lm_head_sample_path(1, 157184, 2560, 29) == 1
+    assert ops.lm_head_sample_path(1, 157184, 2560, 64) == 1
+    assert ops.lm_head_sample_path(1, 4099, 256, 64) == 1
+    assert ops.lm_head_sample_path(4, 157184, 2560, 29) == 0      # several rows: head, then the sampler
+    assert ops.lm_head_sample_path(1, 65, 2560, 64) == 0          # fewer workgroups with rows than top_k
+    assert ops.lm_head_sample_path(1, 157184, 2560, 65) == -1
+
+
+def fused_vs_two_launch(ops, q, s, x_bits, temp, k, p, u):
+    """The one-launch call and the two-launch sampler on the logits it wrote:
+    token, ids and probabilities must be identical."""
+    logits, tok, ids, probs = ops.lm_head_gemv_fp8_sample(q, s, P.to_dev_bf16(x_bits), temp, k, p, P.to_dev(u))
+    t2, i2, p2 = ops.lm_sample_topk_topp(logits, temp, k, p, P.to_dev(u))
+    assert np.array_equal(P.np_(ids), P.np_(i2))
+    assert np.array_equal(P.np_(probs).view(np.uint32), P.np_(p2).view(np.uint32))
+    assert np.array_equal(P.np_(tok), P.np_(t2))
+    return P.np_(logits), P.np_(tok), P.np_(ids), P.np_(probs)
+
+
+@pytest.mark.parametrize("k,temp,p", [(1, 0.6, 0.95), (29, 0.6, 0.95), (64, 1.7, 0.5), (8, 0.05, 1.0)])
+def test_one_launch_equals_two_launch_full_head(ops, full_head, k, temp, p):
+    assert ops.lm_head_sample_path(1, 157184, 2560, k) == 1
+    for j in range(3):
+        x = inputs.normal_bf16((41, k, j), (1, 2560), 1.0)
+        u = inputs.uniform_f32((42, k, j), (1,))
+        lg, tok, ids, probs = fused_vs_two_launch(ops, full_head["q"], full_head["s"], x, temp, k, p, u)
+        check_row(lg[0], temp, k, p, float(u[0]), int(tok[0]), ids[0], probs[0])
+
+
+def test_one_launch_all_equal_logits(ops, full_head):
+    """A zero activation row: every logit is 0, so the top k are rows 0..k-1
+    in order, spread over the first wavefronts of the first workgroup, and
+    the tail's cuts run on maxima that differ only by row."""
+    x = np.zeros((1, 2560), dtype=np.uint16)
+    for k in (1, 29, 64):
+        u = np.array([0.999], dtype=np.float32)
+        lg, tok, ids, probs = fused_vs_two_launch(ops, full_head["q"], full_head["s"], x, 1.0, k, 1.0, u)
+        assert np.all(lg == 0.0)
+        assert list(ids[0]) == list(range(k))
+        assert tok[0] == k - 1
+
+
+def test_one_launch_planted_leaders(ops):
+    """A head whose top rows are planted in one workgroup's rows and tied
+    across workgroups: rows with equal codes give equal logits, so the ranking
+    must fall back to the lower row across chunk and workgroup boundaries."""
+    V, K = 157184, 2560
+    g = np.random.default_rng(9)
+    q = (g.integers(0, 256, size=(V, K)).astype(np.uint8) & 0x87) | 0x20     # |e4m3| small
+    s = np.ones(V, dtype=np.float32)
+    lead = np.array([5, 6, 7, 8, 1000, 64 * 16 * 4 + 5, 150001, 157183])      # several in one group, one in the tail
+    q[lead] = 0x40                                                             # 2.0 everywhere: the largest logits, tied
+    x = F.f64_to_bf16_rne(np.ones((1, K)))
+    qd, sd = P.to_dev(q), P.to_dev(s)
+    for k in (4, 8, 29):
+        u = inputs.uniform_f32((43, k), (1,))
+        lg, tok, ids, probs = fused_vs_two_launch(ops, qd, sd, x, 0.6, k, 0.95, u)
+        assert list(ids[0][:min(k, 8)]) == sorted(lead)[:min(k, 8)]
+        check_row(lg[0], 0.6, k, 0.95, float(u[0]), int(tok[0]), ids[0], probs[0])
+
+
+@pytest.mark.parametrize("V,K,k", [(4099, 256, 64), (2048, 256, 29), (16384 + 7, 256, 29), (70001, 2560, 29)])
+def test_one_launch_other_vocabularies(ops, V, K, k):
+    assert ops.lm_head_sample_path(1, V, K, k) == 1
+    w = inputs.normal_bf16((44, V, K), (V, K), 0.02)
+    q, s = ops.lm_head_quantize_fp8(P.to_dev_bf16(w))
+    x = inputs.normal_bf16((45, V, K), (1, K), 1.0)
+    u = inputs.uniform_f32((46, V, K), (1,))
+    lg, tok, ids, probs = fused_vs_two_launch(ops, q, s, x, 0.6, k, 0.95, u)
+    ok, worst = C.fp_close(lg, OH.head_logits(P.np_(q), P.np_(s), x))
+    assert ok, worst
+    check_row(lg[0], 0.6, k, 0.95, float(u[0]), int(tok[0]), ids[0], probs[0])
+
+
+def test_one_launch_reuses_its_workspace(ops, full_head):
+    """One workspace, many calls with changing inputs: the counter returns to
+    zero and every published maximum is rewritten, so each call equals a call
+    on a fresh workspace."""
+    ws = ops.workspace(int(_lib_mod().load().wsx_lm_head_sample_workspace_bytes(1, 157184, 2560, 29)), "cuda")
+    for j in range(4):
+        x = inputs.normal_bf16((47, j), (1, 2560), 1.0)
+        u = inputs.uniform_f32((48, j), (1,))
+        a = ops.lm_head_gemv_fp8_sample(full_head["q"], full_head["s"], P.to_dev_bf16(x), 0.6, 29, 0.95, P.to_dev(u),
+                                        ws=ws)
+        b = ops.lm_head_gemv_fp8_sample(full_head["q"], full_head["s"], P.to_dev_bf16(x), 0.6, 29, 0.95, P.to_dev(u))
+        for y, z in zip(a, b):
+            assert torch.equal(y, z)
+
+
+def _lib_mod():
+    from weight_streaming_expert_amd import _lib
+    return _lib

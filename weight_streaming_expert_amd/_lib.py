@@ -63,13 +63,14 @@ _PROTOS = {
     "wsx_decode_step_workspace_bytes": [c_int, c_int, c_int, c_int, c_int, c_int],
     "wsx_sample_workspace_bytes": [c_int, c_int, c_int],
     "wsx_lm_head_sample_workspace_bytes": [c_int, c_int, c_int, c_int],
+    "wsx_lm_head_sample_path": [c_int, c_int, c_int, c_int],
     "wsx_status_string": [c_int],
     "wsx_build_info": [],
 }
 _RESTYPES = {"wsx_moe_workspace_bytes": c_size_t, "wsx_lm_head_workspace_bytes": c_size_t,
              "wsx_decode_step_workspace_bytes": c_size_t, "wsx_sample_workspace_bytes": c_size_t,
              "wsx_lm_head_sample_workspace_bytes": c_size_t, "wsx_status_string": c_char_p,
-             "wsx_build_info": c_char_p, "wsx_decode_step_path": c_int}
+             "wsx_build_info": c_char_p, "wsx_decode_step_path": c_int, "wsx_lm_head_sample_path": c_int}
 EXPORTS = tuple(_PROTOS)
 
 _lib = None

@@ -266,9 +266,19 @@ wsx_status lm_sample_topk_topp(const float* logits, int V, int T, float temperat
                                   ws, S(stream)));
 }
 
+static size_t head_sample_region(int T, int V, int top_k) {
+  const size_t s = sample_ws_bytes(T, V, top_k), f = head_sample_fused_ws_bytes(top_k);
+  return T == 1 && f > s ? f : s;
+}
+
 size_t wsx_lm_head_sample_workspace_bytes(int T, int V, int K, int top_k) {
-  const size_t s = wsx_sample_workspace_bytes(T, V, top_k);
-  return s ? align256(head_ws_bytes()) + 256 + s : 0;
+  if (!wsx_sample_workspace_bytes(T, V, top_k)) return 0;
+  return align256(head_ws_bytes()) + 256 + head_sample_region(T, V, top_k);
+}
+
+int wsx_lm_head_sample_path(int T, int V, int K, int top_k) {
+  if (T < 1 || T > WSX_MAX_T || !sample_shape_supported(V, top_k) || !head_shape_supported(0, K)) return -1;
+  return T == 1 ? head_sample_fused_path(V, K, top_k) : 0;
 }
 
 wsx_status lm_head_gemv_fp8_sample(const uint8_t* q, const float* row_scale, int V, int K, const uint16_t* x, int T,
@@ -282,9 +292,18 @@ wsx_status lm_head_gemv_fp8_sample(const uint8_t* q, const float* row_scale, int
   if (!head_shape_supported(0, K)) return WSX_ERR_UNSUPPORTED;
   if (!a16(q) || !a16(x)) return WSX_ERR_ALIGN;
   // workspace: the head's region, 256 bytes for the head's greedy argmax (a
-  // by-product here), then the sampler's candidates
+  // by-product of the two-launch form), then the sampler's region
   const size_t head = align256(head_ws_bytes());
-  if ((st = check_ws(ws, ws_bytes, head + 256 + sample_ws_bytes(T, V, top_k))) != WSX_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, head + 256 + head_sample_region(T, V, top_k))) != WSX_OK) return st;
+  if (T == 1) {
+    // one launch: the head with the selection in its last workgroup
+    bool done = false;
+    const hipError_t e = launch_lm_head_sample_fused(q, row_scale, V, K, x, temperature, top_k, top_p, uniforms, logits,
+                                                     token, topk_ids, topk_probs, ws, (char*)ws + head + 256,
+                                                     S(stream), &done);
+    if (e != hipSuccess) return WSX_ERR_HIP;
+    if (done) return WSX_OK;
+  }
   int32_t* argmax = reinterpret_cast<int32_t*>((char*)ws + head);
   hipError_t e = launch_lm_head(0, q, row_scale, V, K, x, T, 0, nullptr, logits, argmax, ws, S(stream));
   if (e != hipSuccess) return WSX_ERR_HIP;

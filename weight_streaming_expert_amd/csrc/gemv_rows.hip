@@ -17,7 +17,7 @@
 // tokens they are read from LDS.  Row sums are formed by a fixed DPP tree
 // within each 16-lane row, identical for every row, so equal rows give
 // bit-identical logits and ties resolve exactly to the lower index.
-#include "wsx_device.h"
+#include "sample_device.h"
 #include "wsx_internal.h"
 
 namespace wsx {
@@ -241,10 +241,13 @@ __global__ void __launch_bounds__(256) lm_head_kernel(const uint8_t* __restrict_
 
 // The 1-token head ([saipien] "Stop hauling the vocabulary in full
 // precision": the whole head is read for every token) as one 1024-thread
-// workgroup per CU.  Wavefront v of workgroup b takes row groups
-// b * 16 + v + P * 16 * i, so a CU's 16 wavefronts stream neighbouring rows;
-// each keeps the next group's loads in flight while it reduces the current
-// one, and issues its first group's loads before the activations are staged.
+// workgroup per CU.  Wavefront v of workgroup b (of P) takes row groups
+// v * P + b + P * 16 * i: the groups left over after the last full round of
+// P * 16 go to wavefronts of every workgroup, not to the first workgroups
+// alone, so every CU streams the same number of groups to within one.  Each
+// wavefront keeps the next group's loads in flight while it reduces the
+// current one, and issues its first group's loads before the activations are
+// staged.
 // RL lanes per row (RPW = 64 / RL rows per wavefront group), GPL granules per
 // lane.  The activations sit in LDS with granule g at byte g * GS (a stride
 // that lets the RL lanes of a row read their granules without bank
@@ -273,17 +276,157 @@ __device__ __forceinline__ void head_group_load(__amdgpu_buffer_rsrc_t W, const 
   if (WT == W_FP8 && ok && c == 0) g.sc = row_scale[row];
 }
 
-template <int WT, int GPL, int RL>
+// The sampling epilogue of the 1-token head ([ncij] "What happens on a real
+// workload?": temperature, top-p and top-k sampling), fused into its tail.
+// The selection rests on one fact: with the rows split into chunks, the k-th
+// largest chunk maximum tau is at most the k-th largest logit, so every top-k
+// row is >= tau and lies in one of the k chunks whose maximum is >= tau.  Here
+// a chunk is the rows one wavefront streamed (at most 64).  Each wavefront
+// publishes its maximum and each workgroup the largest of its wavefronts'; the
+// last workgroup to finish then
+//   1. takes tau_wg, the k-th largest workgroup maximum: a lower bound of tau
+//      (the k workgroups at or above it each hold a chunk at their own
+//      maximum), so only the chunks of those k workgroups (<= 16 k) can reach
+//      tau;
+//   2. selects tau among those chunk maxima and lists the k chunks at or
+//      above it;
+//   3. reads back those chunks' logits (<= 64 k), keeps the ones >= tau, ranks
+//      them for the top k in order, and draws.
+// Ranks are counted by the whole workgroup over keys staged in LDS
+// (wg_rank_keys); one wavefront draws (sample_draw_wave).  Keys are the 64-bit
+// rank keys of the greedy path (value, then lower row); a NaN logit gets key 0
+// and is never a candidate.  Logits and maxima are written with
+// device-coherent stores so that the last workgroup reads them current on any
+// XCD.
+constexpr int kSampFusedMaxGrid = 512;            // workgroups (so <= 8192 chunks)
+constexpr int kSampFusedMaxChunkRows = 64;        // rows one wavefront may stream
+constexpr int kSampFusedSurvivors = kSampMaxK * kSampFusedMaxChunkRows;
+
+struct HeadSample {
+  RankKey* chunk_max;     // [gridDim.x * 16], by the chunk's first row group
+  RankKey* wg_max;        // [gridDim.x]
+  int k;
+  float temperature, top_p;
+  const float* uniforms;  // [1]
+  int32_t* token;         // [1]
+  int32_t* topk_ids;      // [k] or null
+  float* topk_probs;      // [k] or null
+};
+
+__device__ __forceinline__ RankKey ld_key(const RankKey* base, int i) {
+  const uint2 v = ld_coh8(base, (uint32_t)i * 8);
+  return ((RankKey)v.y << 32) | v.x;
+}
+
+template <int RPW>
+__device__ void head_sample_tail(const HeadSample& P, const float* logits, int V, int NG, int stride) {
+  __shared__ __attribute__((aligned(16))) RankKey gm[kSampFusedMaxGrid + 2];      // workgroup maxima
+  __shared__ __attribute__((aligned(16))) RankKey bk[16 * kSampMaxK + 2];         // chunk maxima >= tau_wg
+  __shared__ int bw[16 * kSampMaxK];                                              // their first row groups
+  __shared__ __attribute__((aligned(16))) RankKey sv[kSampFusedSurvivors + 2];    // rows >= tau
+  __shared__ RankKey top[kSampMaxK];
+  __shared__ int qlist[kSampMaxK];
+  __shared__ RankKey tau_wg, tau;
+  __shared__ int nb, ns;
+  constexpr int kChunkRegs = kSampFusedMaxGrid * 16 / 1024;
+  const int t = threadIdx.x, k = P.k;
+  const int nwg = (int)gridDim.x, nchunk = nwg * 16;
+  // one round of loads: every chunk maximum (in registers), every workgroup
+  // maximum, the uniform
+  RankKey ck[kChunkRegs];
+#pragma unroll
+  for (int r = 0; r < kChunkRegs; ++r) ck[r] = t + 1024 * r < nchunk ? ld_key(P.chunk_max, t + 1024 * r) : 0ull;
+  const RankKey gk = t < nwg ? ld_key(P.wg_max, t) : 0ull;
+  const float u = t < 64 ? P.uniforms[0] : 0.f;
+  // zero fill, so that every list below ends in zeros without a pad
+#pragma unroll
+  for (int r = 0; r < (kSampFusedSurvivors + 2 + 1023) / 1024; ++r)
+    if (t + 1024 * r < kSampFusedSurvivors + 2) sv[t + 1024 * r] = 0ull;
+  bk[t] = 0ull;
+  if (t < kSampMaxK) top[t] = 0ull;
+  if (t <= nwg) gm[t] = t < nwg ? gk : 0ull;
+  if (t == 0) {
+    tau_wg = 1ull;   // no cut unless k workgroups hold a candidate
+    tau = 1ull;
+    nb = 0;
+    ns = 0;
+  }
+  __syncthreads();
+  // 1. tau_wg: the workgroup maximum of rank k - 1 (nonzero maxima are distinct)
+  wg_rank_keys(gm, nwg, [&](int i, int r) {
+    if (r == k - 1 && gm[i] != 0ull) tau_wg = gm[i];
+  });
+  __syncthreads();
+  // 2. the chunk maxima >= tau_wg (at most 16 k)
+  const RankKey tw = tau_wg;
+#pragma unroll
+  for (int r = 0; r < kChunkRegs; ++r)
+    if (ck[r] != 0ull && ck[r] >= tw) {
+      const int pos = atomicAdd(&nb, 1);
+      if (pos < 16 * kSampMaxK) {
+        bk[pos] = ck[r];
+        bw[pos] = t + 1024 * r;
+      }
+    }
+  __syncthreads();
+  // ranked: the first k are the chunks that can hold a top-k row, the k-th is tau
+  const int n_b = min(nb, 16 * kSampMaxK);
+  wg_rank_keys(bk, n_b, [&](int i, int r) {
+    if (r < k) qlist[r] = bw[i];
+    if (r == k - 1) tau = bk[i];
+  });
+  __syncthreads();
+  // 3. the rows of those chunks: the wavefront whose first group is g
+  // streamed groups g + stride * i, RPW rows each; all loads issued first
+  const int n_q = min(n_b, k);
+  const RankKey th = tau;
+  constexpr int kRowRegs = kSampFusedSurvivors / 1024;
+  float lv[kRowRegs];
+  int lrow[kRowRegs];
+#pragma unroll
+  for (int r = 0; r < kRowRegs; ++r) {
+    const int c = t + 1024 * r;
+    const int q = c / kSampFusedMaxChunkRows, s = c % kSampFusedMaxChunkRows;
+    lrow[r] = -1;
+    lv[r] = 0.f;
+    if (q < n_q) {
+      const int grp = qlist[q] + stride * (s / RPW);
+      const int row = grp * RPW + s % RPW;
+      if (grp < NG && row < V) {
+        lrow[r] = row;
+        lv[r] = __uint_as_float(ld_coh4(logits, (uint32_t)row * 4));
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kRowRegs; ++r)
+    if (lrow[r] >= 0 && lv[r] == lv[r]) {
+      const RankKey key = rank_key(lv[r], lrow[r]);
+      if (key >= th) {
+        const int pos = atomicAdd(&ns, 1);
+        if (pos < kSampFusedSurvivors) sv[pos] = key;
+      }
+    }
+  __syncthreads();
+  wg_rank_keys(sv, min(ns, kSampFusedSurvivors), [&](int i, int r) {
+    if (r < k) top[r] = sv[i];
+  });
+  __syncthreads();
+  if (t < 64) sample_draw_wave(t < k ? top[t] : 0ull, k, P.temperature, P.top_p, u, P.token, P.topk_ids, P.topk_probs);
+}
+
+template <int WT, int GPL, int RL, bool SAMPLE>
 __global__ void __launch_bounds__(1024) lm_head_wide_kernel(const uint8_t* __restrict__ W,
                                                             const float* __restrict__ row_scale, int V, int K,
                                                             const uint16_t* __restrict__ x, float* __restrict__ logits,
                                                             int32_t* __restrict__ argmax, unsigned* counter,
-                                                            unsigned long long* best) {
+                                                            unsigned long long* best, HeadSample smp) {
   constexpr int EPG = WTraits<WT>::EPG, DW = EPG / 2, RPW = 64 / RL, NW = 16;
   constexpr int GS = (WT == W_FP8) ? 48 : 16;   // LDS bytes per activation granule
   extern __shared__ __attribute__((aligned(16))) uint8_t xsb[];
   __shared__ float wv_[NW];
   __shared__ int wi_[NW];
+  __shared__ RankKey wk_[NW];
   __shared__ int flag;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, c = lane % RL;
   const int G = K / EPG;
@@ -291,23 +434,24 @@ __global__ void __launch_bounds__(1024) lm_head_wide_kernel(const uint8_t* __res
   const __amdgpu_buffer_rsrc_t Wr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(W), 0, 0x7FFFFFFF, 0x00020000);
   const int NG = (V + RPW - 1) / RPW;
   const int stride = (int)gridDim.x * NW;
-  int grp = (int)blockIdx.x * NW + wave;
+  const int first = wave * (int)gridDim.x + (int)blockIdx.x;
+  int grp = first < NG ? first : -1;
   // x first (one 16-byte chunk of 8 bf16 per thread, K <= 8192), then the
   // first group: loads complete in issue order, so the staging below waits
   // for x alone and the group stays in flight across the barrier
   uint4 xv = make_uint4(0, 0, 0, 0);
   if (t < K / 8) xv = ld16(x + 8 * t);
   HeadGroup<WT, GPL, RL> cur;
-  if (grp < NG) head_group_load<WT, GPL, RL>(Wr, row_scale, V, G, row_bytes, grp, cur);
+  if (grp >= 0) head_group_load<WT, GPL, RL>(Wr, row_scale, V, G, row_bytes, grp, cur);
   issue_here();
   if (t < K / 8) *reinterpret_cast<uint4*>(xsb + (8 * t / EPG) * GS + (8 * t % EPG) * 2) = xv;
   lds_barrier();
   float bv = -INFINITY;
   int bi = 0x7FFFFFFF;
-  while (grp < NG) {
+  while (grp >= 0) {
     HeadGroup<WT, GPL, RL> nxt;
-    const int ng = grp + stride;
-    if (ng < NG) head_group_load<WT, GPL, RL>(Wr, row_scale, V, G, row_bytes, ng, nxt);
+    const int ng = grp + stride < NG ? grp + stride : -1;
+    if (ng >= 0) head_group_load<WT, GPL, RL>(Wr, row_scale, V, G, row_bytes, ng, nxt);
     issue_here();
     float acc = 0.f;
 #pragma unroll
@@ -315,10 +459,10 @@ __global__ void __launch_bounds__(1024) lm_head_wide_kernel(const uint8_t* __res
       const int g = c + RL * j;
       if (g < G) {
         uint32_t xp[DW];
-        const uint4* src = reinterpret_cast<const uint4*>(xsb + g * GS);
+        const uint4* src4 = reinterpret_cast<const uint4*>(xsb + g * GS);
 #pragma unroll
         for (int d = 0; d < DW / 4; ++d) {
-          const uint4 v = src[d];
+          const uint4 v = src4[d];
           xp[4 * d] = v.x; xp[4 * d + 1] = v.y; xp[4 * d + 2] = v.z; xp[4 * d + 3] = v.w;
         }
         acc += granule_dot<WT>(cur.w[j], xp);
@@ -327,30 +471,48 @@ __global__ void __launch_bounds__(1024) lm_head_wide_kernel(const uint8_t* __res
     acc = sum16(acc);
     if constexpr (RL == 32) acc += __shfl_xor(acc, 16);
     const int row = grp * RPW + lane / RL;
+    const float l = (WT == W_FP8) ? acc * cur.sc : acc;
     if (c == 0 && row < V) {
-      const float l = (WT == W_FP8) ? acc * cur.sc : acc;
-      if (logits) logits[row] = l;
+      if constexpr (SAMPLE) st_coh4(logits, (uint32_t)row * 4, __float_as_uint(l));
+      else if (logits) logits[row] = l;
       if (better(l, row, bv, bi)) { bv = l; bi = row; }
     }
     cur = nxt;
     grp = ng;
   }
   wave_argmax(bv, bi);
-  if (lane == 0) { wv_[wave] = bv; wi_[wave] = bi; }
-  lds_barrier();
-  if (t == 0) {
-    float v = wv_[0];
-    int i = wi_[0];
-    for (int q = 1; q < NW; ++q)
-      if (better(wv_[q], wi_[q], v, i)) { v = wv_[q]; i = wi_[q]; }
-    const RankKey key = (v == v) ? rank_key(v, i) : 0ull;   // a NaN never wins
-    __hip_atomic_fetch_max(best, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  if (!last_block_arrived(counter, gridDim.x, &flag)) return;
-  if (t == 0) {
-    const RankKey b = __hip_atomic_load(best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(best, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    argmax[0] = b == 0ull ? -1 : key_id(b);
+  if constexpr (SAMPLE) {
+    // this chunk's maximum (0 when it streamed no row that is a number)
+    const RankKey m = bi != 0x7FFFFFFF ? rank_key(bv, bi) : 0ull;
+    if (lane == 0) {
+      wk_[wave] = m;
+      st_coh8(smp.chunk_max, (uint32_t)first * 8, make_uint2((unsigned)m, (unsigned)(m >> 32)));
+    }
+    lds_barrier();
+    if (t == 0) {
+      RankKey wm = wk_[0];
+      for (int q = 1; q < NW; ++q) wm = wk_[q] > wm ? wk_[q] : wm;
+      st_coh8(smp.wg_max, (uint32_t)blockIdx.x * 8, make_uint2((unsigned)wm, (unsigned)(wm >> 32)));
+    }
+    if (!last_block_arrived(counter, gridDim.x, &flag)) return;
+    head_sample_tail<RPW>(smp, logits, V, NG, stride);
+  } else {
+    if (lane == 0) { wv_[wave] = bv; wi_[wave] = bi; }
+    lds_barrier();
+    if (t == 0) {
+      float v = wv_[0];
+      int i = wi_[0];
+      for (int q = 1; q < NW; ++q)
+        if (better(wv_[q], wi_[q], v, i)) { v = wv_[q]; i = wi_[q]; }
+      const RankKey key = (v == v) ? rank_key(v, i) : 0ull;   // a NaN never wins
+      __hip_atomic_fetch_max(best, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (!last_block_arrived(counter, gridDim.x, &flag)) return;
+    if (t == 0) {
+      const RankKey b = __hip_atomic_load(best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(best, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      argmax[0] = b == 0ull ? -1 : key_id(b);
+    }
   }
 }
 
@@ -623,11 +785,6 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ lrow, int E
 // to this wavefront's LDS slots (rank-major, zeros elsewhere), and each of the
 // 8 PW candidates is ranked against the others through readlane broadcasts.
 // Leaves the k (logit, id) pairs in rank order in rv / rid.
-__device__ __forceinline__ RankKey readlane_key(RankKey v, int j) {
-  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(v >> 32), j);
-  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)v, j);
-  return ((RankKey)hi << 32) | lo;
-}
 
 template <int PW>
 __device__ __forceinline__ void wave_topk(const float* __restrict__ lrow, int E, int k, RankKey* cand, float* rv,
@@ -973,9 +1130,10 @@ int head_grid(int V) {
 
 // The wide 1-token head for the shapes it is compiled for: one workgroup per
 // CU; weights addressed with 32-bit offsets, so the head must be below 2 GiB.
+// smp non-null: the sampling variant (FP8 only; see head_sample_fused_fits).
 static hipError_t launch_head_wide(int wt, const void* W, const float* s, int V, int K, const uint16_t* x,
                                    float* logits, int32_t* argmax, unsigned* counter, unsigned long long* best,
-                                   hipStream_t st, bool* done) {
+                                   hipStream_t st, bool* done, const HeadSample* smp = nullptr) {
   *done = false;
   if ((size_t)V * K * (wt == W_FP8 ? 1 : 2) >= ((size_t)1 << 31)) return hipSuccess;
   int dev = 0, cus = 0;
@@ -986,17 +1144,80 @@ static hipError_t launch_head_wide(int wt, const void* W, const float* s, int V,
   const size_t lds = (size_t)(K / epg) * gs;
 #define WSX_WIDE(WTV, GPLV, RLV)                                                                                   \
   {                                                                                                              \
-    lm_head_wide_kernel<WTV, GPLV, RLV><<<cus, 1024, lds, st>>>((const uint8_t*)W, s, V, K, x, logits, argmax,   \
-                                                                 counter, best);                                 \
+    lm_head_wide_kernel<WTV, GPLV, RLV, false><<<cus, 1024, lds, st>>>((const uint8_t*)W, s, V, K, x, logits,    \
+                                                                        argmax, counter, best, HeadSample{});    \
     *done = true;                                                                                                \
     return hipGetLastError();                                                                                    \
   }
-  if (wt == W_FP8 && K == 2560) WSX_WIDE(W_FP8, 10, 16)
-  if (wt == W_FP8 && K == 256) WSX_WIDE(W_FP8, 1, 16)
+#define WSX_WIDE_S(GPLV, RLV)                                                                                      \
+  {                                                                                                              \
+    if (smp)                                                                                                     \
+      lm_head_wide_kernel<W_FP8, GPLV, RLV, true><<<cus, 1024, lds, st>>>((const uint8_t*)W, s, V, K, x, logits, \
+                                                                          argmax, counter, best, *smp);          \
+    else                                                                                                         \
+      lm_head_wide_kernel<W_FP8, GPLV, RLV, false><<<cus, 1024, lds, st>>>((const uint8_t*)W, s, V, K, x,        \
+                                                                           logits, argmax, counter, best,        \
+                                                                           HeadSample{});                        \
+    *done = true;                                                                                                \
+    return hipGetLastError();                                                                                    \
+  }
+  if (wt == W_FP8 && K == 2560) WSX_WIDE_S(10, 16)
+  if (wt == W_FP8 && K == 256) WSX_WIDE_S(1, 16)
+  if (smp) return hipSuccess;
   if (wt == W_BF16 && K == 2560) WSX_WIDE(W_BF16, 10, 32)
   if (wt == W_BF16 && K == 256) WSX_WIDE(W_BF16, 1, 32)
 #undef WSX_WIDE
+#undef WSX_WIDE_S
   return hipSuccess;
+}
+
+// chunk maxima, then workgroup maxima
+size_t head_sample_fused_ws_bytes(int) { return (size_t)kSampFusedMaxGrid * (16 + 1) * sizeof(RankKey); }
+
+// Whether the sampling variant of the wide FP8 head takes (V, K, top_k) on a
+// device of `cus` compute units: the wide head's shapes, at most
+// kSampFusedMaxGrid workgroups, every wavefront streaming at most 64 rows, and
+// at least top_k workgroups with rows (the selection's first cut).
+bool head_sample_fused_fits(int V, int K, int top_k, int cus) {
+  if (K != 2560 && K != 256) return false;
+  if ((size_t)V * K >= ((size_t)1 << 31) || V < 1) return false;
+  if (cus < 1 || cus > kSampFusedMaxGrid || top_k < 1 || top_k > kSampMaxK || top_k > V) return false;
+  constexpr int RPW = 4;                               // rows per group of the FP8 wide head (16 lanes a row)
+  const int NG = (V + RPW - 1) / RPW;
+  const int stride = cus * 16;
+  const int groups_per_wave = (NG + stride - 1) / stride;
+  const int wgs_with_rows = min(cus, (NG + 15) / 16);
+  return groups_per_wave * RPW <= kSampFusedMaxChunkRows && wgs_with_rows >= top_k;
+}
+
+int head_sample_fused_path(int V, int K, int top_k) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return head_sample_fused_fits(V, K, top_k, cus) ? 1 : 0;
+}
+
+hipError_t launch_lm_head_sample_fused(const void* W, const float* s, int V, int K, const uint16_t* x,
+                                       float temperature, int top_k, float top_p, const float* uniforms,
+                                       float* logits, int32_t* token, int32_t* topk_ids, float* topk_probs,
+                                       void* head_ws, void* sample_ws, hipStream_t st, bool* done) {
+  *done = false;
+  if (!head_sample_fused_path(V, K, top_k)) return hipSuccess;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return hipSuccess;
+  HeadSample smp;
+  smp.chunk_max = reinterpret_cast<RankKey*>(sample_ws);
+  smp.wg_max = smp.chunk_max + (size_t)cus * 16;
+  smp.k = top_k;
+  smp.temperature = temperature;
+  smp.top_p = top_p;
+  smp.uniforms = uniforms;
+  smp.token = token;
+  smp.topk_ids = topk_ids;
+  smp.topk_probs = topk_probs;
+  return launch_head_wide(W_FP8, W, s, V, K, x, logits, nullptr, reinterpret_cast<unsigned*>(head_ws), nullptr, st,
+                          done, &smp);
 }
 
 hipError_t launch_lm_head(int wt, const void* W, const float* s, int V, int K, const uint16_t* x, int T, int norm,

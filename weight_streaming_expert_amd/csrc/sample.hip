@@ -24,14 +24,13 @@
 //     top-k key is a candidate >= tau of one of the (at most k) chunks whose
 //     maximum is >= tau: only those k * k candidates are read, in one round
 //     of loads.  Ranking the survivors against each other gives the top k in
-//     order; one lane then runs the sequential sums and the draw.
-#include "wsx_device.h"
+//     order; one wavefront then runs the sums in rank order and the draw.
+#include "sample_device.h"
 #include "wsx_internal.h"
 
 namespace wsx {
 
 constexpr int kSampChunk = 64;          // logits per chunk: one wavefront
-constexpr int kSampMaxK = 64;
 constexpr int kSampMaxChunks = 8192;    // V <= 8191 * 64; also bounds the k * k survivors
 
 __global__ void __launch_bounds__(256) sample_candidates_kernel(const float* __restrict__ logits, int V, int k,
@@ -58,16 +57,6 @@ __global__ void __launch_bounds__(256) sample_candidates_kernel(const float* __r
   if (lane >= nvalid && lane < k) out[lane] = 0ull;
 }
 
-// rank of m among buf[0..n) (n even; keys are distinct apart from zeros)
-__device__ __forceinline__ int lds_rank(const RankKey* buf, int n, RankKey m) {
-  int r = 0;
-  for (int j = 0; j < n; j += 2) {
-    const ulonglong2 kk = *reinterpret_cast<const ulonglong2*>(buf + j);
-    r += (int)(kk.x > m) + (int)(kk.y > m);
-  }
-  return r;
-}
-
 __global__ void __launch_bounds__(1024) sample_select_kernel(const RankKey* __restrict__ cand,
                                                             const RankKey* __restrict__ maxima, int nchunk, int k,
                                                             float temperature, float top_p,
@@ -76,15 +65,13 @@ __global__ void __launch_bounds__(1024) sample_select_kernel(const RankKey* __re
                                                             float* __restrict__ topk_probs) {
   __shared__ __attribute__((aligned(16))) RankKey buf[kSampMaxChunks];
   __shared__ RankKey top[kSampMaxK];
-  __shared__ float ev[kSampMaxK];
-  __shared__ float cs_m;
   __shared__ int qlist[kSampMaxK];
   __shared__ unsigned hist[256];
   __shared__ RankKey tau;
-  __shared__ int ns, nq, msel, sel_digit, sel_need, sel_count;
+  __shared__ int ns, nq, sel_digit, sel_need, sel_count;
   const int t = blockIdx.x;
   const RankKey* ct = cand + (size_t)t * nchunk * k;
-  const float u = threadIdx.x == 0 ? uniforms[t] : 0.f;   // in flight from the start
+  const float u = threadIdx.x < 64 ? uniforms[t] : 0.f;   // in flight from the start
   if (threadIdx.x == 0) {
     tau = 1ull;   // no cut when there are fewer than k chunks
     ns = 0;
@@ -180,49 +167,13 @@ __global__ void __launch_bounds__(1024) sample_select_kernel(const RankKey* __re
   const int n = min(ns, kSampMaxChunks);
   if (threadIdx.x == 0 && (n & 1)) buf[n] = 0ull;
   __syncthreads();
-  const int n2 = (n + 1) & ~1;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const RankKey m = buf[i];
-    const int r = lds_rank(buf, n2, m);
-    if (r < k) top[r] = m;
-  }
+  wg_rank_keys(buf, n, [&](int i, int r) {
+    if (r < k) top[r] = buf[i];
+  });
   __syncthreads();
-  const float z0 = key_value(top[0]);
-  if ((int)threadIdx.x < k) ev[threadIdx.x] = expf((key_value(top[threadIdx.x]) - z0) / temperature);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    // the running sums in rank order, held in registers (k <= 64)
-    float c[kSampMaxK];
-    float acc = 0.f;
-#pragma unroll
-    for (int i = 0; i < kSampMaxK; ++i) {
-      if (i < k) acc += ev[i];
-      c[i] = acc;
-    }
-    const float thr = top_p * acc;
-    int m = k - 1;
-#pragma unroll
-    for (int i = kSampMaxK - 1; i >= 0; --i)
-      if (i < k && c[i] >= thr) m = i;   // the first such i
-    float mass = c[0];
-#pragma unroll
-    for (int i = 1; i < kSampMaxK; ++i)
-      if (i == m) mass = c[i];
-    const float target = u * mass;
-    int j = m;
-#pragma unroll
-    for (int i = kSampMaxK - 1; i >= 0; --i)
-      if (i <= m && c[i] > target) j = i;   // the first such i
-    msel = m;
-    cs_m = mass;
-    token[t] = key_id(top[j]);
-  }
-  __syncthreads();
-  if ((int)threadIdx.x < k) {
-    const int i = threadIdx.x, m = msel;
-    if (topk_ids) topk_ids[(size_t)t * k + i] = key_id(top[i]);
-    if (topk_probs) topk_probs[(size_t)t * k + i] = i <= m ? ev[i] / cs_m : 0.f;
-  }
+  if (threadIdx.x < 64)
+    sample_draw_wave((int)threadIdx.x < k ? top[threadIdx.x] : 0ull, k, temperature, top_p, u, token + t,
+                     topk_ids ? topk_ids + (size_t)t * k : nullptr, topk_probs ? topk_probs + (size_t)t * k : nullptr);
 }
 
 size_t sample_ws_bytes(int T, int V, int k) {

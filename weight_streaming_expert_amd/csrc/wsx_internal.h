@@ -71,4 +71,15 @@ hipError_t launch_sample(const float* logits, int V, int T, float temperature, i
                          const float* uniforms, int32_t* token, int32_t* topk_ids, float* topk_probs, void* ws,
                          hipStream_t st);
 
+// gemv_rows.hip: the 1-token FP8 head with the sampler fused into its tail.
+// head_ws: the head's region (its counters first); sample_ws: at least
+// head_sample_fused_ws_bytes(top_k).  *done = false (nothing launched) when the
+// shape or device does not fit (head_sample_fused_path == 0).
+size_t head_sample_fused_ws_bytes(int k);
+int head_sample_fused_path(int V, int K, int top_k);
+hipError_t launch_lm_head_sample_fused(const void* W, const float* s, int V, int K, const uint16_t* x,
+                                       float temperature, int top_k, float top_p, const float* uniforms,
+                                       float* logits, int32_t* token, int32_t* topk_ids, float* topk_probs,
+                                       void* head_ws, void* sample_ws, hipStream_t st, bool* done);
+
 }  // namespace wsx

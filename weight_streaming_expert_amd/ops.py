@@ -232,8 +232,16 @@ def lm_sample_topk_topp(logits, temperature, top_k, top_p, uniforms, ws=None):
     return tok, ids, probs
 
 
+def lm_head_sample_path(T, V, K, top_k):
+    """1: lm_head_gemv_fp8_sample is one launch (the sampler in the head's
+    tail) on the current device; 0: three launches; -1: unsupported sizes."""
+    return int(_lib.load().wsx_lm_head_sample_path(T, V, K, top_k))
+
+
 def lm_head_gemv_fp8_sample(q, row_scale, x, temperature, top_k, top_p, uniforms, ws=None):
-    """FP8 head then the sampler on its logits.  Returns (logits, token, ids, probs)."""
+    """FP8 head with the sampler on its logits (fused into the head's tail for
+    one token where lm_head_sample_path says so).  Returns (logits, token, ids,
+    probs)."""
     _chk(q, torch.uint8, "q")
     _chk(row_scale, torch.float32, "row_scale")
     _chk(x, torch.bfloat16, "x")
