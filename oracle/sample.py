@@ -28,7 +28,9 @@ given are binary32 (a head oracle's fp64 logits rounded once).
 Pins (tests/test_oracle_sample.py): top_k = 1 and tiny top_p give the argmax;
 with top_k = V and top_p = 1 the interval widths are scipy's softmax of
 logits / temperature; the kept set is the smallest high-probability set of
-mass >= top_p, by brute force over all subsets of a tiny vocabulary; a worked
+mass >= top_p, by brute force over all subsets of a tiny vocabulary, and so
+are cumulative_bounds' kept ranks at top_p < 1 after a top-k cut, with widths
+from an fp64 softmax renormalised over the kept set; a worked
 example by hand (tests/golden/sampling_example.json); u -> 0 gives rank 0 and
 u -> 1 the last kept rank; a constant added to every logit changes nothing;
 sampling frequencies over a fine grid of u match the probabilities.
@@ -77,16 +79,6 @@ def sample_row(logits_row, temperature, top_k, top_p, u):
             j = i
             break
     return int(ids[j]), ids, p
-
-
-def sample(logits, temperature, top_k, top_p, uniforms):
-    """sample_row over the rows of logits [T][V] with uniforms [T]."""
-    logits = np.atleast_2d(logits)
-    out = [sample_row(logits[t], temperature, top_k, top_p, uniforms[t]) for t in range(logits.shape[0])]
-    tokens = np.array([o[0] for o in out], dtype=np.int64)
-    ids = np.stack([o[1] for o in out])
-    probs = np.stack([o[2] for o in out])
-    return tokens, ids, probs
 
 
 def cumulative_bounds(logits_row, temperature, top_k, top_p):

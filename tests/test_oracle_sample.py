@@ -90,6 +90,37 @@ def test_top_p_keeps_the_smallest_heavy_set(seed):
     assert set(ids[p > 0].tolist()) == best
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_cumulative_bounds_below_top_p_one(seed):
+    """cumulative_bounds at top_p < 1, after a top-k cut: the kept ranks are the
+    brute-force smallest heavy set of the top k (found by trying every subset
+    of the renormalised top-k probabilities), and each interval's width is that
+    token's probability renormalised over the kept set, from an fp64 softmax."""
+    V, k = 9, 7
+    g = np.random.default_rng(300 + seed)
+    z = (g.standard_normal(V) * 2).astype(np.float32)
+    top_p = float(g.uniform(0.3, 0.95))
+    T = 0.7
+    top = np.argsort(-z.astype(np.float64), kind="stable")[:k]
+    q = softmax(z[top].astype(np.float64) / T)          # the top k, renormalised
+    best = None
+    for r in range(1, k + 1):
+        for sub in itertools.combinations(range(k), r):
+            rest = [i for i in range(k) if i not in sub]
+            if q[list(sub)].sum() >= top_p and (not rest or q[list(sub)].min() > q[rest].max()):
+                best = sorted(sub)
+                break
+        if best is not None:
+            break
+    kept, lo, hi = Sm.cumulative_bounds(z, T, k, top_p)
+    assert sorted(kept.tolist()) == sorted(top[best].tolist())
+    want = q[best] / q[best].sum()
+    order = [best[list(top[best]).index(i)] for i in kept]   # the oracle's rank order
+    assert np.allclose(hi - lo, q[order] / q[best].sum(), rtol=1e-12, atol=1e-15)
+    assert lo[0] == 0.0 and abs(hi[-1] - 1.0) < 1e-12 and np.all(np.diff(hi) > 0)
+    assert np.isclose(want.sum(), 1.0)
+
+
 def test_u_limits_and_shift_invariance():
     z = (np.round(rand_logits(3, 5000) * 1024) / 1024).astype(np.float32)   # 2^-10 grid: z + 16 is exact
     for k, tp in ((29, 0.95), (8, 0.5), (64, 1.0)):
