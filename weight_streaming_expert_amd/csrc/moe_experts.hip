@@ -151,6 +151,99 @@ __global__ void __launch_bounds__(256) moe_gateup_kernel(const uint16_t* __restr
   }
 }
 
+// The 1-token gate/up with every load issued before the first wait: the
+// slot's list entry, the activations (held in registers) and, once the expert
+// is known, all of the workgroup's weights; only then are the activations
+// staged in LDS.  The arithmetic is moe_gateup_kernel's for T = 1.
+template <int NJ>
+__global__ void __launch_bounds__(256) moe_gateup1_kernel(const uint16_t* __restrict__ x, int H, int I, int E,
+                                                          int max_slots, const uint8_t* __restrict__ w13c,
+                                                          const uint8_t* __restrict__ w13s,
+                                                          const uint8_t* __restrict__ sh13c,
+                                                          const uint8_t* __restrict__ sh13s,
+                                                          const int32_t* __restrict__ expert_list,
+                                                          float* __restrict__ a_out) {
+  constexpr int XC = 2;   // 16-byte activation chunks per thread: H <= 8 * 256 * XC
+  const int slot = blockIdx.y;
+  int n_active = expert_list[0];
+  const int e_slot = slot < max_slots - 1 ? expert_list[1 + slot] : -1;
+  uint4 xv[XC];
+#pragma unroll
+  for (int q = 0; q < XC; ++q) {
+    const int i = threadIdx.x + 256 * q;
+    xv[q] = i < H / 8 ? ld16(x + 8 * i) : make_uint4(0, 0, 0, 0);
+  }
+  n_active = n_active < 0 ? 0 : (n_active > max_slots - 1 ? max_slots - 1 : n_active);
+  const bool has_sh = sh13c != nullptr;
+  const int i0 = blockIdx.x * 16;
+  const uint8_t *C = nullptr, *S = nullptr;
+  bool ok = false;
+  if (slot < n_active) {
+    ok = e_slot >= 0 && e_slot < E;
+    if (ok) {
+      C = w13c + (size_t)e_slot * ((size_t)2 * I * (H / 2));
+      S = w13s + (size_t)e_slot * ((size_t)2 * I * (H / 32));
+    }
+  } else if (slot == n_active && has_sh) {
+    ok = true;
+    C = sh13c;
+    S = sh13s;
+  }
+  if (!ok) {
+    // inactive slot past the list: nothing to do; bad id: contribute zeros
+    if (slot < n_active + (has_sh ? 1 : 0))
+      for (int i = threadIdx.x; i < 16; i += 256) a_out[(size_t)slot * I + i0 + i] = 0.f;
+    return;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane >> 4, c = lane & 15;
+  const int NB = H / 32;
+  const size_t rowc = H / 2, rows = H / 32;
+  uint4 cw[2][NJ];
+  uint32_t sb[2][NJ];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const int ri = i0 + 4 * wave + 2 * st + (r & 1);
+    const int row = (r < 2) ? ri : I + ri;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int b = c + 16 * j;
+      cw[st][j] = (b < NB) ? ld16(C + row * rowc + (size_t)b * 16) : make_uint4(0, 0, 0, 0);
+      sb[st][j] = (b < NB) ? (uint32_t)S[row * rows + b] : 127u;
+    }
+  }
+  issue_here();
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
+#pragma unroll
+  for (int q = 0; q < XC; ++q) {
+    const int i = threadIdx.x + 256 * q;
+    if (i < H / 8) reinterpret_cast<uint4*>(xs)[i] = xv[q];
+  }
+  lds_barrier();
+  const uint32_t* xs32 = reinterpret_cast<const uint32_t*>(xs);
+  uint32_t xr[NJ][16];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int b = c + 16 * j;
+#pragma unroll
+    for (int d = 0; d < 16; ++d) xr[j][d] = (b < NB) ? xs32[b * 16 + d] : 0u;
+  }
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int b = c + 16 * j;
+      if (b >= NB) continue;
+      acc = fmaf(mx_block_dot(cw[st][j], xr[j]), e8m0_to_f32(sb[st][j]), acc);
+    }
+    const int ri = i0 + 4 * wave + 2 * st + (r & 1);
+    const float sum = sum16(acc);
+    const float up = __shfl_xor(sum, 32);
+    if (r < 2 && c == 0) a_out[(size_t)slot * I + ri] = silu(sum) * up;
+  }
+}
+
 // ---------------------------------------------------------------- gate/up on the matrix cores
 
 // Gate/up + SwiGLU for T tokens with v_mfma_f32_16x16x32_bf16: workgroup
@@ -399,6 +492,106 @@ __global__ void __launch_bounds__(256) moe_down_kernel(int H, int I, int E, int 
       if (out_h2) out_h2[o] = h;
     }
   }
+}
+
+// The 1-token down + combine + residual with every weight load issued first:
+// each wavefront reads the list entries of its slots (s = wave + 4 i, i <
+// MAXS) and issues all of those slots' weight loads, and only then are the
+// activations staged in LDS.  The arithmetic and the summation order are
+// moe_down_kernel's for T = 1.
+template <int NJD, int MAXS>
+__global__ void __launch_bounds__(256) moe_down1_kernel(int H, int I, int E, int max_slots,
+                                                        const uint8_t* __restrict__ w2c, const uint8_t* __restrict__ w2s,
+                                                        const uint8_t* __restrict__ sh2c, const uint8_t* __restrict__ sh2s,
+                                                        const int32_t* __restrict__ expert_list,
+                                                        const float* __restrict__ slot_w, const float* __restrict__ a_in,
+                                                        const uint16_t* __restrict__ residual, float* __restrict__ out_y,
+                                                        uint16_t* __restrict__ out_h, uint16_t* __restrict__ out_h2) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int n_active = expert_list[0];
+  int eid[MAXS];
+  float wt[MAXS];
+#pragma unroll
+  for (int i = 0; i < MAXS; ++i) {
+    const int s = wave + 4 * i;
+    eid[i] = s < max_slots - 1 ? expert_list[1 + s] : -1;
+    wt[i] = s < max_slots - 1 ? slot_w[s] : 1.0f;
+  }
+  n_active = n_active < 0 ? 0 : (n_active > max_slots - 1 ? max_slots - 1 : n_active);
+  const bool has_sh = sh2c != nullptr;
+  const int nslots = n_active + (has_sh ? 1 : 0);
+  const int r = lane >> 3, c = lane & 7;
+  const int n0 = blockIdx.x * 8;
+  const int row = n0 + r;
+  const int NBd = I / 32;
+  const size_t rowc = I / 2, rows = I / 32;
+  uint4 cw[MAXS][NJD];
+  uint32_t sb[MAXS][NJD];
+  bool use[MAXS];
+#pragma unroll
+  for (int i = 0; i < MAXS; ++i) {
+    const int s = wave + 4 * i;
+    const uint8_t *C = nullptr, *S = nullptr;
+    use[i] = false;
+    if (s < n_active) {
+      use[i] = eid[i] >= 0 && eid[i] < E;
+      if (use[i]) {
+        C = w2c + (size_t)eid[i] * ((size_t)H * (I / 2));
+        S = w2s + (size_t)eid[i] * ((size_t)H * (I / 32));
+      }
+    } else if (s == n_active && has_sh) {
+      use[i] = true;
+      C = sh2c;
+      S = sh2s;
+      wt[i] = 1.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < NJD; ++j) {
+      const int b = c + 8 * j;
+      cw[i][j] = (use[i] && b < NBd) ? ld16(C + row * rowc + (size_t)b * 16) : make_uint4(0, 0, 0, 0);
+      sb[i][j] = (use[i] && b < NBd) ? (uint32_t)S[row * rows + b] : 127u;
+    }
+  }
+  issue_here();
+  extern __shared__ __attribute__((aligned(16))) float as[];
+  stage_to_lds<256, 7>(a_in, as, nslots * I / 4);
+  __syncthreads();
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXS; ++i) {
+    if (!use[i]) continue;
+    const int s = wave + 4 * i;
+#pragma unroll
+    for (int j = 0; j < NJD; ++j) {
+      const int b = c + 8 * j;
+      if (b >= NBd) continue;
+      const float scale = e8m0_to_f32(sb[i][j]);
+      const float* ap = as + (size_t)s * I + (size_t)b * 32;
+      float av[32];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float4 v = reinterpret_cast<const float4*>(ap)[q];
+        av[4 * q] = v.x; av[4 * q + 1] = v.y; av[4 * q + 2] = v.z; av[4 * q + 3] = v.w;
+      }
+      acc = fmaf(wt[i] * scale, mx_block_dot_f32(cw[i][j], av), acc);
+    }
+  }
+  __shared__ float part[4][8];
+  const float v = sum8(acc);
+  if (c == 0) part[wave][r] = v;
+  __syncthreads();
+  if (threadIdx.x < 8) {
+    const int rr = threadIdx.x;
+    const float y = ((part[0][rr] + part[1][rr]) + part[2][rr]) + part[3][rr];
+    const size_t o = (size_t)n0 + rr;
+    if (out_y) out_y[o] = y;
+    if (residual) {
+      const uint16_t h = f32_to_bf16_rne(bf16_bits_to_f32(residual[o]) + y);
+      if (out_h) out_h[o] = h;
+      if (out_h2) out_h2[o] = h;
+    }
+  }
+  (void)nslots;
 }
 
 // ---------------------------------------------------------------- down for several tokens
@@ -784,6 +977,20 @@ hipError_t launch_gateup(const uint16_t* x, int T, int H, int I, int E, int k, c
       case 4: return launch_gateup_mfma_t<4>(x, H, I, E, max_slots, w13c, w13s, sh13c, sh13s, el, a, st);
     }
   }
+  if (T == 1 && H <= 8 * 256 * 2) {
+    const int nj = (H / 32 + 15) / 16;
+    dim3 grid(I / 16, max_slots);
+    const size_t lds = (size_t)H * 2;
+#define WSX_G1_CASE(N)                                                                                     \
+  case N:                                                                                                  \
+    moe_gateup1_kernel<N><<<grid, 256, lds, st>>>(x, H, I, E, max_slots, w13c, w13s, sh13c, sh13s, el, a); \
+    return hipGetLastError();
+    switch (nj) {
+      WSX_G1_CASE(1) WSX_G1_CASE(2) WSX_G1_CASE(4) WSX_G1_CASE(5) WSX_G1_CASE(8) WSX_G1_CASE(16)
+      default: return hipErrorInvalidValue;
+    }
+#undef WSX_G1_CASE
+  }
   switch (T) {
     case 1: return launch_gateup_t<1>(x, H, I, E, max_slots, w13c, w13s, sh13c, sh13s, el, a, st);
     case 2: return launch_gateup_t<2>(x, H, I, E, max_slots, w13c, w13s, sh13c, sh13s, el, a, st);
@@ -879,6 +1086,20 @@ hipError_t launch_down(int T, int H, int I, int E, int k, const uint8_t* w2c, co
     }
   }
   const bool alds = (size_t)max_slots * T * I * 4 <= kDownLdsLimit;
+  if (T == 1 && alds && max_slots <= 12 && (size_t)max_slots * I / 4 <= (size_t)256 * 7) {
+    const int njd = (I / 32 + 7) / 8;
+    const size_t lds = (size_t)max_slots * I * 4;
+#define WSX_D1_CASE(N)                                                                                           \
+  case N:                                                                                                        \
+    moe_down1_kernel<N, 3><<<H / 8, 256, lds, st>>>(H, I, E, max_slots, w2c, w2s, sh2c, sh2s, el, sw, a, res, y, h, \
+                                                    h2);                                                          \
+    return hipGetLastError();
+    switch (njd) {
+      WSX_D1_CASE(1) WSX_D1_CASE(2) WSX_D1_CASE(3) WSX_D1_CASE(4) WSX_D1_CASE(6) WSX_D1_CASE(8)
+      default: return hipErrorInvalidValue;
+    }
+#undef WSX_D1_CASE
+  }
 #define WSX_DT(TV)                                                                                           \
   case TV:                                                                                                   \
     return alds ? launch_down_t<TV, true>(H, I, E, max_slots, w2c, w2s, sh2c, sh2s, el, sw, a, res, y, h, h2, st) \
