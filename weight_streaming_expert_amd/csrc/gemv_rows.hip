@@ -524,10 +524,11 @@ __global__ void __launch_bounds__(1024) lm_head_wide_kernel(const uint8_t* __res
 // of them) as a small dense contraction on
 // v_mfma_f32_16x16x32_bf16: 16 head rows x 32 K values x 16 token columns
 // (columns past T are zero).  E4M3 codes are decoded to bf16 exactly; the row
-// scale multiplies the fp32 sum.  One 1024-thread workgroup per CU; the work
+// scale multiplies the fp32 sum.  Four 256-thread workgroups per CU; the work
 // unit of a wavefront is (16-row tile, quarter of K), and the four wavefronts
-// v..v+3 (v = 0 mod 4) of a workgroup take the four quarters of one tile, so
-// their partial tiles meet in LDS and are added in quarter order.  The MFMA's
+// of a workgroup take the four quarters of one tile (so the tile's 40 KB are
+// read together), their partial tiles meet in LDS and are added in quarter
+// order; the barrier of each tile couples only those four wavefronts.  The MFMA's
 // 32-wide K slice is a permutation of K: lane (r, q) takes the 16-code granule
 // at K offset 64 j + 16 q of its quarter and feeds codes 0-7 and 8-15 to two
 // MFMAs, and the token columns take the same activations from LDS.  Each
@@ -562,12 +563,13 @@ __device__ __forceinline__ void head_unit_load(__amdgpu_buffer_rsrc_t W, __amdgp
 }
 
 template <int T, int NS>   // NS: 64-value K steps per quarter of K
-__global__ void __launch_bounds__(1024) lm_head_mfma_kernel(const uint8_t* __restrict__ W,
+__global__ void __launch_bounds__(256) lm_head_mfma_kernel(const uint8_t* __restrict__ W,
                                                             const float* __restrict__ row_scale, int V, int K,
                                                             const uint16_t* __restrict__ x, float* __restrict__ logits,
                                                             int32_t* __restrict__ argmax, unsigned* counter,
                                                             float* part_v, int* part_i) {
-  constexpr int NW = 16;
+  constexpr int NW = 4;
+  constexpr int XPT = 5;   // 16-byte activation chunks per thread: T K / 8 <= 256 XPT
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ float wv_[NW][T];
   __shared__ int wi_[NW][T];
@@ -584,12 +586,12 @@ __global__ void __launch_bounds__(1024) lm_head_mfma_kernel(const uint8_t* __res
   const int stride = (int)gridDim.x * NW;
   const int iters = (units + stride - 1) / stride;
   int u = (int)blockIdx.x * NW + wave;
-  // x first (T*K/8 16-byte chunks, two per thread at most), then the first unit
-  uint4 xv[2];
+  // x first (T*K/8 16-byte chunks, XPT per thread at most), then the first unit
+  uint4 xv[XPT];
   const int nx = T * K / 8;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = t + 1024 * i;
+  for (int i = 0; i < XPT; ++i) {
+    const int c = t + 256 * i;
     xv[i] = c < nx ? ld16(x + 8 * c) : make_uint4(0, 0, 0, 0);
   }
   uint4 cw[NS];
@@ -597,8 +599,8 @@ __global__ void __launch_bounds__(1024) lm_head_mfma_kernel(const uint8_t* __res
   if (u < units) head_unit_load<NS>(Wr, Sr, V, K, u, cw, cs);
   issue_here();
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = t + 1024 * i;
+  for (int i = 0; i < XPT; ++i) {
+    const int c = t + 256 * i;
     if (c < nx) *reinterpret_cast<uint4*>(xs + (c / (K / 8)) * KS + (c % (K / 8)) * 8) = xv[i];
   }
   lds_barrier();
@@ -1234,13 +1236,13 @@ hipError_t launch_lm_head(int wt, const void* W, const float* s, int V, int K, c
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus >= 1) {
-      const int grid = cus < kHeadMaxGrid ? cus : kHeadMaxGrid;
+      const int grid = 4 * cus < kHeadMaxGrid ? 4 * cus : kHeadMaxGrid;   // four 256-thread workgroups per CU
       float* pv = reinterpret_cast<float*>((char*)ws + 256);
       int* pi = reinterpret_cast<int*>((char*)ws + 256 + (size_t)kHeadMaxGrid * WSX_MAX_T * 4);
-      const size_t lds = (((size_t)T * (K + 8) * 2 + 15) & ~(size_t)15) + (size_t)2 * 16 * 64 * 16;
+      const size_t lds = (((size_t)T * (K + 8) * 2 + 15) & ~(size_t)15) + (size_t)2 * 4 * 64 * 16;
 #define WSX_MF(TV) \
   if (T == TV) { \
-    lm_head_mfma_kernel<TV, 10><<<grid, 1024, lds, st>>>((const uint8_t*)W, s, V, K, x, logits, argmax, counter, pv, pi); \
+    lm_head_mfma_kernel<TV, 10><<<grid, 256, lds, st>>>((const uint8_t*)W, s, V, K, x, logits, argmax, counter, pv, pi); \
     return hipGetLastError(); \
   }
       WSX_MF(2) WSX_MF(3) WSX_MF(4)
