@@ -142,6 +142,47 @@ __device__ __forceinline__ void load_x_regs(const uint32_t* xs32, int G, uint32_
 
 // ---------------------------------------------------------------- LM head
 
+// The argmax over the per-workgroup partials (value, row) of the head's T
+// tokens, by a 256-thread last workgroup: each thread loads its (at most
+// kHeadMaxGrid / 256) partials of every token at once, so the tail is one
+// coherent round trip; then the wavefront and workgroup reductions (ties to
+// the lower row, so the result does not depend on the order).
+template <int T>
+__device__ __forceinline__ void head_partials_argmax(const float* part_v, const int* part_i, int nb, float (*wv)[T],
+                                                     int (*wi)[T], int32_t* argmax) {
+  constexpr int PB = kHeadMaxGrid / 256;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float ov[T][PB];
+  int oi[T][PB];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int j = 0; j < PB; ++j) {
+      const int b = (int)threadIdx.x + 256 * j;
+      ov[t][j] = b < nb ? __uint_as_float(ld_coh4(part_v, (uint32_t)(b * T + t) * 4)) : -INFINITY;
+      oi[t][j] = b < nb ? (int)ld_coh4(part_i, (uint32_t)(b * T + t) * 4) : 0x7FFFFFFF;
+    }
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    float v = -INFINITY;
+    int i = 0x7FFFFFFF;
+#pragma unroll
+    for (int j = 0; j < PB; ++j)
+      if (better(ov[t][j], oi[t][j], v, i)) { v = ov[t][j]; i = oi[t][j]; }
+    wave_argmax(v, i);
+    if (lane == 0) { wv[wave][t] = v; wi[wave][t] = i; }
+  }
+  __syncthreads();
+  if (threadIdx.x < T) {
+    const int t = threadIdx.x;
+    float v = wv[0][t];
+    int i = wi[0][t];
+    for (int w = 1; w < 4; ++w)
+      if (better(wv[w][t], wi[w][t], v, i)) { v = wv[w][t]; i = wi[w][t]; }
+    argmax[t] = i;
+  }
+}
+
 template <int WT, int T, int GPL>
 __global__ void __launch_bounds__(256) lm_head_kernel(const uint8_t* __restrict__ W, const float* __restrict__ row_scale,
                                                       int V, int K, const uint16_t* __restrict__ x, int norm,
@@ -213,27 +254,7 @@ __global__ void __launch_bounds__(256) lm_head_kernel(const uint8_t* __restrict_
     st_dev(part_i + (size_t)blockIdx.x * T + t, i);
   }
   if (!last_block_arrived(counter, gridDim.x, &flag)) return;
-#pragma unroll
-  for (int t = 0; t < T; ++t) {
-    float v = -INFINITY;
-    int i = 0x7FFFFFFF;
-    for (int b = threadIdx.x; b < (int)gridDim.x; b += NT) {
-      float ov = ld_dev(part_v + (size_t)b * T + t);
-      int oi = ld_dev(part_i + (size_t)b * T + t);
-      if (better(ov, oi, v, i)) { v = ov; i = oi; }
-    }
-    wave_argmax(v, i);
-    if (lane == 0) { wv_[wave][t] = v; wi_[wave][t] = i; }
-  }
-  __syncthreads();
-  if (threadIdx.x < T) {
-    const int t = threadIdx.x;
-    float v = wv_[0][t];
-    int i = wi_[0][t];
-    for (int w = 1; w < 4; ++w)
-      if (better(wv_[w][t], wi_[w][t], v, i)) { v = wv_[w][t]; i = wi_[w][t]; }
-    argmax[t] = i;
-  }
+  head_partials_argmax<T>(part_v, part_i, (int)gridDim.x, wv_, wi_, argmax);
 }
 
 
@@ -672,20 +693,7 @@ __global__ void __launch_bounds__(256) lm_head_mfma_kernel(const uint8_t* __rest
     st_dev(part_i + (size_t)blockIdx.x * T + t, i);
   }
   if (!last_block_arrived(counter, gridDim.x, &flag)) return;
-  if (wave == 0) {
-#pragma unroll
-    for (int tt = 0; tt < T; ++tt) {
-      float v = -INFINITY;
-      int i = 0x7FFFFFFF;
-      for (int b = lane; b < (int)gridDim.x; b += 64) {
-        const float ov = ld_dev(part_v + (size_t)b * T + tt);
-        const int oi = ld_dev(part_i + (size_t)b * T + tt);
-        if (better(ov, oi, v, i)) { v = ov; i = oi; }
-      }
-      wave_argmax(v, i);
-      if (lane == 0) argmax[tt] = i;
-    }
-  }
+  head_partials_argmax<T>(part_v, part_i, (int)gridDim.x, wv_, wi_, argmax);
 }
 
 // ---------------------------------------------------------------- router + top-k

@@ -62,6 +62,41 @@ __device__ __forceinline__ bool slot_expert(int slot, int n_active, bool has_sh,
   return false;
 }
 
+// Sum, in group order, of the ng partials part[(g T + t) H + n] (written by
+// other workgroups with device-coherent stores): the loads go out eight at a
+// time, so the tail costs one coherent round trip per eight groups, not one
+// per group.
+__device__ __forceinline__ float sum_group_partials(const float* part, int ng, int T, int H, int t, int n) {
+  float y = 0.f;
+  for (int g0 = 0; g0 < ng; g0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      v[j] = g0 + j < ng ? __uint_as_float(ld_coh4(part, (uint32_t)(((size_t)(g0 + j) * T + t) * H + n) * 4)) : 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (g0 + j < ng) y += v[j];
+  }
+  return y;
+}
+
+// slot_expert with the slot's list entry already loaded (read beside the
+// active count, so the two loads share one round trip): e_slot is
+// expert_list[1 + slot] for slot < max_slots - 1, anything otherwise.
+__device__ __forceinline__ bool slot_expert_pre(int slot, int n_active, bool has_sh, int E, int e_slot,
+                                                const uint8_t* wc, const uint8_t* ws_, const uint8_t* shc,
+                                                const uint8_t* shs, size_t c_stride, size_t s_stride,
+                                                const uint8_t** C, const uint8_t** S) {
+  if (slot < n_active) {
+    if (e_slot < 0 || e_slot >= E) return false;
+    *C = wc + (size_t)e_slot * c_stride;
+    *S = ws_ + (size_t)e_slot * s_stride;
+    return true;
+  }
+  if (slot == n_active && has_sh) { *C = shc; *S = shs; return true; }
+  return false;
+}
+
 // ---------------------------------------------------------------- gate/up + SwiGLU
 
 template <int T, int NJ>
@@ -617,14 +652,16 @@ __global__ void __launch_bounds__(256) moe_down_grouped_kernel(
     const float* __restrict__ slot_w, const float* __restrict__ a_in, const uint16_t* __restrict__ residual,
     float* __restrict__ out_y, uint16_t* __restrict__ out_h, uint16_t* __restrict__ out_h2, float* part,
     unsigned* counters) {
+  const int s = 4 * (int)blockIdx.y + (int)(threadIdx.x >> 6);
   int n_active = expert_list[0];
+  const int e_slot = s < max_slots - 1 ? expert_list[1 + s] : -1;
   n_active = n_active < 0 ? 0 : (n_active > max_slots - 1 ? max_slots - 1 : n_active);
   const bool has_sh = sh2c != nullptr;
   const int nslots = n_active + (has_sh ? 1 : 0);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kg = lane & 7, rq = lane >> 3;
   const int n0 = blockIdx.x * kDnRows;
-  const int g = blockIdx.y, s = 4 * g + wave;
+  const int g = blockIdx.y;
   const int NB = I / 32;
   const int lstride = NB * 36;   // floats per token row in LDS
   extern __shared__ __attribute__((aligned(16))) float as[];   // [4][T][lstride]
@@ -638,8 +675,8 @@ __global__ void __launch_bounds__(256) moe_down_grouped_kernel(
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[r][t] = 0.f;
   const uint8_t *C = nullptr, *S = nullptr;
-  const bool active = s < nslots && slot_expert(s, n_active, has_sh, E, expert_list, w2c, w2s, sh2c, sh2s,
-                                                (size_t)H * (I / 2), (size_t)H * (I / 32), &C, &S);
+  const bool active = s < nslots && slot_expert_pre(s, n_active, has_sh, E, e_slot, w2c, w2s, sh2c, sh2s,
+                                                    (size_t)H * (I / 2), (size_t)H * (I / 32), &C, &S);
   if (active) {
     // weights first (their latency overlaps the staging)
     const size_t rowc = I / 2, rows = I / 32;
@@ -735,8 +772,7 @@ __global__ void __launch_bounds__(256) moe_down_grouped_kernel(
   if (!last_block_arrived(counters + blockIdx.x * 16, gridDim.y, &flag)) return;
   if (threadIdx.x < kDnRows * T) {
     const int t = threadIdx.x / kDnRows, rr = threadIdx.x % kDnRows;
-    float y = 0.f;
-    for (int gg = 0; gg < (int)gridDim.y; ++gg) y += ld_dev(part + ((size_t)gg * T + t) * H + n0 + rr);
+    const float y = sum_group_partials(part, (int)gridDim.y, T, H, t, n0 + rr);
     const size_t o = (size_t)t * H + n0 + rr;
     if (out_y) out_y[o] = y;
     if (residual) {
@@ -888,8 +924,7 @@ __global__ void __launch_bounds__(256) moe_down_sparse_kernel(
   if (!last_block_arrived(counters + blockIdx.x * 16, gridDim.y, &flag)) return;
   for (int i = threadIdx.x; i < T * kDnRows; i += 256) {
     const int t = i / kDnRows, rr = i % kDnRows;
-    float y = 0.f;
-    for (int gg = 0; gg < (int)gridDim.y; ++gg) y += ld_dev(part + ((size_t)gg * T + t) * H + n0 + rr);
+    const float y = sum_group_partials(part, (int)gridDim.y, T, H, t, n0 + rr);
     const size_t o = (size_t)t * H + n0 + rr;
     if (out_y) out_y[o] = y;
     if (residual) {
