@@ -411,18 +411,27 @@ __global__ void __launch_bounds__(256) moe_gateup_mfma_g_kernel(const uint16_t* 
       sc[h][j] = ok ? e8m0_to_f32(S[r * rows + b]) : 0.f;
     }
   }
-  __shared__ float red[4][2][16][WSX_MAX_T_MOE];
+  // rows of 20 floats: the four rows 4q + r that one store touches then
+  // fall 16 banks apart (a 16-float row put them all in the same banks)
+  __shared__ float red[4][2][16][20];
+  static_assert(WSX_MAX_T_MOE <= 20, "reduction tile columns");
   f32x4_t dg = {0.f, 0.f, 0.f, 0.f}, du = {0.f, 0.f, 0.f, 0.f};
   const int col = row;   // B operand: lane (col, q), token col
+  // every activation chunk of this wavefront's quarter, issued together with
+  // the weights above (one round trip, not one per step)
+  uint4 xa[NQ][4];
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
     const int b = b0 + 4 * j + q;
-    const bool ok = b < NB;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      xa[j][m] = (col < T && b < NB) ? ld16(x + (size_t)col * H + b * 32 + m * 8) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      uint4 xv = make_uint4(0, 0, 0, 0);
-      if (col < T && ok) xv = ld16(x + (size_t)col * H + b * 32 + m * 8);
-      const bf16x8_t bx = __builtin_bit_cast(bf16x8_t, xv);
+      const bf16x8_t bx = __builtin_bit_cast(bf16x8_t, xa[j][m]);
       const uint32_t wg = m == 0 ? cw[0][j].x : m == 1 ? cw[0][j].y : m == 2 ? cw[0][j].z : cw[0][j].w;
       const uint32_t wu = m == 0 ? cw[1][j].x : m == 1 ? cw[1][j].y : m == 2 ? cw[1][j].z : cw[1][j].w;
       dg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4x8_to_bf16x8(wg, sc[0][j]), bx, dg, 0, 0, 0);
@@ -442,6 +451,118 @@ __global__ void __launch_bounds__(256) moe_gateup_mfma_g_kernel(const uint16_t* 
     const float g = ((red[0][0][rr][t] + red[1][0][rr][t]) + red[2][0][rr][t]) + red[3][0][rr][t];
     const float u = ((red[0][1][rr][t] + red[1][1][rr][t]) + red[2][1][rr][t]) + red[3][1][rr][t];
     a_out[((size_t)slot * T + t) * I + i0 + rr] = silu(g) * u;
+  }
+}
+
+// The same contraction for 5..16 tokens with four 16-row tiles per
+// workgroup: each wavefront keeps its quarter of K of all T token columns in
+// registers (loaded once, with the first tile's weights) and reuses it for
+// the workgroup's tiles, whose gate/up rows stream one tile ahead; so the
+// activations are read once per 64 rows instead of once per 16.  Each tile's
+// four quarter sums meet in LDS (double-buffered, one barrier per tile) and are
+// added in wavefront order, as in moe_gateup_mfma_g_kernel.
+template <int NQ, int NTI>
+__global__ void __launch_bounds__(256) moe_gateup_mfma_mt_kernel(const uint16_t* __restrict__ x, int T, int H, int I,
+                                                                 int E, int max_slots, const uint8_t* __restrict__ w13c,
+                                                                 const uint8_t* __restrict__ w13s,
+                                                                 const uint8_t* __restrict__ sh13c,
+                                                                 const uint8_t* __restrict__ sh13s,
+                                                                 const int32_t* __restrict__ expert_list,
+                                                                 float* __restrict__ a_out) {
+  const int slot = blockIdx.y;
+  int n_active = expert_list[0];
+  const int e_slot = slot < max_slots - 1 ? expert_list[1 + slot] : -1;
+  n_active = n_active < 0 ? 0 : (n_active > max_slots - 1 ? max_slots - 1 : n_active);
+  const bool has_sh = sh13c != nullptr;
+  const int ibase = blockIdx.x * 16 * NTI;
+  const uint8_t *C, *S;
+  if (!slot_expert_pre(slot, n_active, has_sh, E, e_slot, w13c, w13s, sh13c, sh13s, (size_t)2 * I * (H / 2),
+                       (size_t)2 * I * (H / 32), &C, &S)) {
+    if (slot < n_active + (has_sh ? 1 : 0))
+      for (int i = threadIdx.x; i < 16 * NTI * T; i += 256) {
+        const int ii = ibase + i % (16 * NTI);
+        if (ii < I) a_out[((size_t)slot * T + i / (16 * NTI)) * I + ii] = 0.f;
+      }
+    return;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = lane & 15, q = lane >> 4;
+  const int NB = H / 32;
+  const int b0 = wave * 4 * NQ;
+  const size_t rowc = H / 2, rows = H / 32;
+  const int col = row;   // B operand: lane (col, q), token col
+  auto load_tile = [&](int i0, uint4 (&cw)[2][NQ], float (&sc)[2][NQ]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = h * I + i0 + row;
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) {
+        const int b = b0 + 4 * j + q;
+        const bool ok = b < NB;
+        cw[h][j] = ok ? ld16(C + r * rowc + (size_t)b * 16) : make_uint4(0, 0, 0, 0);
+        sc[h][j] = ok ? e8m0_to_f32(S[r * rows + b]) : 0.f;
+      }
+    }
+  };
+  uint4 cw[2][NQ];
+  float sc[2][NQ];
+  load_tile(ibase, cw, sc);
+  uint4 xa[NQ][4];
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const int b = b0 + 4 * j + q;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      xa[j][m] = (col < T && b < NB) ? ld16(x + (size_t)col * H + b * 32 + m * 8) : make_uint4(0, 0, 0, 0);
+  }
+  // rows of 20 floats: the four rows 4q + r that one store touches fall 16
+  // banks apart
+  __shared__ float red[2][4][2][16][20];
+  static_assert(WSX_MAX_T_MOE <= 20, "reduction tile columns");
+#pragma unroll 1
+  for (int ti = 0; ti < NTI; ++ti) {
+    const int i0 = ibase + 16 * ti;
+    if (i0 >= I) break;   // the same in every thread
+    uint4 nw[2][NQ];
+    float ns[2][NQ];
+    if (ti + 1 < NTI && i0 + 16 < I) load_tile(i0 + 16, nw, ns);
+    issue_here();
+    f32x4_t dg = {0.f, 0.f, 0.f, 0.f}, du = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const bf16x8_t bx = __builtin_bit_cast(bf16x8_t, xa[j][m]);
+        const uint32_t wg = m == 0 ? cw[0][j].x : m == 1 ? cw[0][j].y : m == 2 ? cw[0][j].z : cw[0][j].w;
+        const uint32_t wu = m == 0 ? cw[1][j].x : m == 1 ? cw[1][j].y : m == 2 ? cw[1][j].z : cw[1][j].w;
+        dg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4x8_to_bf16x8(wg, sc[0][j]), bx, dg, 0, 0, 0);
+        du = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4x8_to_bf16x8(wu, sc[1][j]), bx, du, 0, 0, 0);
+      }
+    }
+    float (*rb)[2][16][20] = red[ti & 1];
+    if (col < T) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        rb[wave][0][4 * q + r][col] = dg[r];
+        rb[wave][1][4 * q + r][col] = du[r];
+      }
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < 16 * T) {
+      const int rr = threadIdx.x % 16, t = threadIdx.x / 16;
+      const float g = ((rb[0][0][rr][t] + rb[1][0][rr][t]) + rb[2][0][rr][t]) + rb[3][0][rr][t];
+      const float u = ((rb[0][1][rr][t] + rb[1][1][rr][t]) + rb[2][1][rr][t]) + rb[3][1][rr][t];
+      a_out[((size_t)slot * T + t) * I + i0 + rr] = silu(g) * u;
+    }
+    if (ti + 1 < NTI) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+          cw[h][j] = nw[h][j];
+          sc[h][j] = ns[h][j];
+        }
+    }
   }
 }
 
@@ -802,14 +923,16 @@ __global__ void __launch_bounds__(256) moe_down_sparse_kernel(
     float* __restrict__ out_y, uint16_t* __restrict__ out_h, uint16_t* __restrict__ out_h2, float* part,
     unsigned* counters) {
   constexpr int TC = 4;   // tokens per pass
+  const int s = 4 * (int)blockIdx.y + (int)(threadIdx.x >> 6);
   int n_active = expert_list[0];
+  const int e_slot = s < max_slots - 1 ? expert_list[1 + s] : -1;
   n_active = n_active < 0 ? 0 : (n_active > max_slots - 1 ? max_slots - 1 : n_active);
   const bool has_sh = sh2c != nullptr;
   const int nslots = n_active + (has_sh ? 1 : 0);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kg = lane & 7, rq = lane >> 3;
   const int n0 = blockIdx.x * kDnRows;
-  const int g = blockIdx.y, s = 4 * g + wave;
+  const int g = blockIdx.y;
   const int NB = I / 32;
   const int lstride = NB * 36;   // floats per token row in LDS
   extern __shared__ __attribute__((aligned(16))) float as[];   // [4][TC][lstride]
@@ -818,8 +941,8 @@ __global__ void __launch_bounds__(256) moe_down_sparse_kernel(
   float* aw = as + (size_t)wave * TC * lstride;
   for (int i = lane; i < WSX_MAX_T_MOE * kDnRows; i += 64) yw[wave][i / kDnRows][i % kDnRows] = 0.f;
   const uint8_t *C = nullptr, *S = nullptr;
-  const bool active = s < nslots && slot_expert(s, n_active, has_sh, E, expert_list, w2c, w2s, sh2c, sh2s,
-                                                (size_t)H * (I / 2), (size_t)H * (I / 32), &C, &S);
+  const bool active = s < nslots && slot_expert_pre(s, n_active, has_sh, E, e_slot, w2c, w2s, sh2c, sh2s,
+                                                    (size_t)H * (I / 2), (size_t)H * (I / 32), &C, &S);
   if (active) {
     const size_t rowc = I / 2, rows = I / 32;
     uint4 cw[NKB][4];
@@ -846,15 +969,26 @@ __global__ void __launch_bounds__(256) moe_down_sparse_kernel(
         wt[j] = tok[j] >= 0 ? readlane_f(wl, tok[j]) : 0.f;
         tm &= tm - 1;
       }
-      // these tokens' activations -> LDS (32-value blocks at a 36-float stride)
+      // these tokens' activations -> LDS (32-value blocks at a 36-float
+      // stride), every load issued before the first store (I <= 256 NKB)
       const int nq = I / 4;
+      float4 av4[TC][NKB];
 #pragma unroll
       for (int j = 0; j < TC; ++j) {
-        if (tok[j] < 0) continue;
-        const float4* src = reinterpret_cast<const float4*>(a_in + ((size_t)s * T + tok[j]) * I);
-        for (int q4 = lane; q4 < nq; q4 += 64)
-          *reinterpret_cast<float4*>(aw + j * lstride + dpos(4 * q4)) = src[q4];
+        const float4* src = reinterpret_cast<const float4*>(a_in + ((size_t)s * T + (tok[j] < 0 ? 0 : tok[j])) * I);
+#pragma unroll
+        for (int m = 0; m < NKB; ++m) {
+          const int q4 = lane + 64 * m;
+          av4[j][m] = (tok[j] >= 0 && q4 < nq) ? src[q4] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
       }
+#pragma unroll
+      for (int j = 0; j < TC; ++j)
+#pragma unroll
+        for (int m = 0; m < NKB; ++m) {
+          const int q4 = lane + 64 * m;
+          if (tok[j] >= 0 && q4 < nq) *reinterpret_cast<float4*>(aw + j * lstride + dpos(4 * q4)) = av4[j][m];
+        }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -987,10 +1121,12 @@ static hipError_t launch_gateup_g(const uint16_t* x, int T, int H, int I, int E,
                                   const uint8_t* w13s, const uint8_t* sh13c, const uint8_t* sh13s, const int32_t* el,
                                   float* a, hipStream_t st) {
   const int nq = (H / 32 + 15) / 16;
-  dim3 grid(I / 16, max_slots);
-#define WSX_GG_CASE(N)                                                                                        \
-  case N:                                                                                                     \
-    moe_gateup_mfma_g_kernel<N><<<grid, 256, 0, st>>>(x, T, H, I, E, max_slots, w13c, w13s, sh13c, sh13s, el, a); \
+  constexpr int kTiles = 4;   // 16-row tiles per workgroup
+  dim3 grid((I / 16 + kTiles - 1) / kTiles, max_slots);
+#define WSX_GG_CASE(N)                                                                                              \
+  case N:                                                                                                           \
+    moe_gateup_mfma_mt_kernel<N, kTiles><<<grid, 256, 0, st>>>(x, T, H, I, E, max_slots, w13c, w13s, sh13c, sh13s, \
+                                                               el, a);                                              \
     break;
   switch (nq) {
     WSX_GG_CASE(1) WSX_GG_CASE(2) WSX_GG_CASE(4) WSX_GG_CASE(5) WSX_GG_CASE(8) WSX_GG_CASE(16)
