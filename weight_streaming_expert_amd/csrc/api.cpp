@@ -178,8 +178,8 @@ wsx_status moe_expert_gemv_mxfp4(const uint16_t* x, const uint8_t* w13_codes, co
   float* a = reinterpret_cast<float*>((char*)ws + L.a);
   float* part = reinterpret_cast<float*>((char*)ws + L.part);
   unsigned* dcnt = reinterpret_cast<unsigned*>((char*)ws + L.dcnt);
-  hipError_t e = launch_gateup(x, T, H, I, E, k, w13_codes, w13_scales, sh13_codes, sh13_scales, expert_list, a,
-                               S(stream));
+  hipError_t e = launch_gateup(x, T, H, I, E, k, w13_codes, w13_scales, sh13_codes, sh13_scales, expert_list, slot_w,
+                               a, S(stream));
   if (e != hipSuccess) return WSX_ERR_HIP;
   return hip_status(launch_down(T, H, I, E, k, w2_codes, w2_scales, sh2_codes, sh2_scales, expert_list, slot_w, a,
                                 residual, out_y, out_h, nullptr, part, dcnt, S(stream)));
@@ -428,7 +428,7 @@ wsx_status moe_decode_step(const uint16_t* h_in, int T, const wsx_moe_stack* sk,
     if (e != hipSuccess) return WSX_ERR_HIP;
     e = launch_gateup(u, T, H, I, E, k, sk->w13_codes + (size_t)l * c13, sk->w13_scales + (size_t)l * s13,
                       sh ? sk->sh13_codes + (size_t)l * sc13 : nullptr, sh ? sk->sh13_scales + (size_t)l * ss13 : nullptr,
-                      el, a, s);
+                      el, sw, a, s);
     if (e != hipSuccess) return WSX_ERR_HIP;
     e = launch_down(T, H, I, E, k, sk->w2_codes + (size_t)l * c2, sk->w2_scales + (size_t)l * s2,
                     sh ? sk->sh2_codes + (size_t)l * sc2 : nullptr, sh ? sk->sh2_scales + (size_t)l * ss2 : nullptr,

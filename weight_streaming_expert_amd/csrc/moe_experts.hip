@@ -468,6 +468,7 @@ __global__ void __launch_bounds__(256) moe_gateup_mfma_mt_kernel(const uint16_t*
                                                                  const uint8_t* __restrict__ sh13c,
                                                                  const uint8_t* __restrict__ sh13s,
                                                                  const int32_t* __restrict__ expert_list,
+                                                                 const float* __restrict__ slot_w,
                                                                  float* __restrict__ a_out) {
   const int slot = blockIdx.y;
   int n_active = expert_list[0];
@@ -475,6 +476,11 @@ __global__ void __launch_bounds__(256) moe_gateup_mfma_mt_kernel(const uint16_t*
   n_active = n_active < 0 ? 0 : (n_active > max_slots - 1 ? max_slots - 1 : n_active);
   const bool has_sh = sh13c != nullptr;
   const int ibase = blockIdx.x * 16 * NTI;
+  // a routed slot serves only the tokens routed to it (nonzero weight in its
+  // row of slot_w): the down stage reads no other column, so the others are
+  // neither loaded nor meaningful (they come out 0); the shared expert serves all
+  const int colw = (int)(threadIdx.x & 15);
+  const float wcol = (slot < n_active && colw < T) ? slot_w[(size_t)slot * T + colw] : 1.0f;
   const uint8_t *C, *S;
   if (!slot_expert_pre(slot, n_active, has_sh, E, e_slot, w13c, w13s, sh13c, sh13s, (size_t)2 * I * (H / 2),
                        (size_t)2 * I * (H / 32), &C, &S)) {
@@ -507,13 +513,14 @@ __global__ void __launch_bounds__(256) moe_gateup_mfma_mt_kernel(const uint16_t*
   uint4 cw[2][NQ];
   float sc[2][NQ];
   load_tile(ibase, cw, sc);
+  const bool col_used = col < T && wcol != 0.f;
   uint4 xa[NQ][4];
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
     const int b = b0 + 4 * j + q;
 #pragma unroll
     for (int m = 0; m < 4; ++m)
-      xa[j][m] = (col < T && b < NB) ? ld16(x + (size_t)col * H + b * 32 + m * 8) : make_uint4(0, 0, 0, 0);
+      xa[j][m] = (col_used && b < NB) ? ld16(x + (size_t)col * H + b * 32 + m * 8) : make_uint4(0, 0, 0, 0);
   }
   // rows of 20 floats: the four rows 4q + r that one store touches fall 16
   // banks apart
@@ -1119,14 +1126,14 @@ static hipError_t launch_gateup_mfma_t(const uint16_t* x, int H, int I, int E, i
 
 static hipError_t launch_gateup_g(const uint16_t* x, int T, int H, int I, int E, int max_slots, const uint8_t* w13c,
                                   const uint8_t* w13s, const uint8_t* sh13c, const uint8_t* sh13s, const int32_t* el,
-                                  float* a, hipStream_t st) {
+                                  const float* sw, float* a, hipStream_t st) {
   const int nq = (H / 32 + 15) / 16;
   constexpr int kTiles = 4;   // 16-row tiles per workgroup
   dim3 grid((I / 16 + kTiles - 1) / kTiles, max_slots);
 #define WSX_GG_CASE(N)                                                                                              \
   case N:                                                                                                           \
     moe_gateup_mfma_mt_kernel<N, kTiles><<<grid, 256, 0, st>>>(x, T, H, I, E, max_slots, w13c, w13s, sh13c, sh13s, \
-                                                               el, a);                                              \
+                                                               el, sw, a);                                          \
     break;
   switch (nq) {
     WSX_GG_CASE(1) WSX_GG_CASE(2) WSX_GG_CASE(4) WSX_GG_CASE(5) WSX_GG_CASE(8) WSX_GG_CASE(16)
@@ -1138,9 +1145,9 @@ static hipError_t launch_gateup_g(const uint16_t* x, int T, int H, int I, int E,
 
 hipError_t launch_gateup(const uint16_t* x, int T, int H, int I, int E, int k, const uint8_t* w13c,
                          const uint8_t* w13s, const uint8_t* sh13c, const uint8_t* sh13s, const int32_t* el,
-                         float* a, hipStream_t st) {
+                         const float* sw, float* a, hipStream_t st) {
   const int max_slots = T * k + 1;
-  if (T > WSX_MAX_T) return launch_gateup_g(x, T, H, I, E, max_slots, w13c, w13s, sh13c, sh13s, el, a, st);
+  if (T > WSX_MAX_T) return launch_gateup_g(x, T, H, I, E, max_slots, w13c, w13s, sh13c, sh13s, el, sw, a, st);
   if (T >= 2) {
     switch (T) {
       case 2: return launch_gateup_mfma_t<2>(x, H, I, E, max_slots, w13c, w13s, sh13c, sh13s, el, a, st);

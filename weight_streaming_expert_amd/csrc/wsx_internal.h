@@ -29,7 +29,7 @@ hipError_t launch_router(int router_dtype, const void* W, int E, int K, int k, c
 bool experts_shape_supported(int H, int I);
 hipError_t launch_gateup(const uint16_t* x, int T, int H, int I, int E, int k, const uint8_t* w13c,
                          const uint8_t* w13s, const uint8_t* sh13c, const uint8_t* sh13s, const int32_t* el,
-                         float* a, hipStream_t st);
+                         const float* sw, float* a, hipStream_t st);
 hipError_t launch_down(int T, int H, int I, int E, int k, const uint8_t* w2c, const uint8_t* w2s,
                        const uint8_t* sh2c, const uint8_t* sh2s, const int32_t* el, const float* sw, const float* a,
                        const uint16_t* res, float* y, uint16_t* h, uint16_t* h2, float* part, unsigned* counters,
