@@ -88,6 +88,47 @@ def test_tiny_handmade_expert_list_and_no_shared(ops, tiny):
         assert hd is None
 
 
+def test_one_token_handmade_lists_and_workspace_reuse(ops, tiny):
+    """One token with a caller-built expert list: one workspace serves calls
+    with 2, 1 and 0 routed slots and an out-of-range id (which contributes
+    nothing), with and without the shared expert, each checked against the
+    oracle and against the same call on a fresh workspace, bit for bit."""
+    wl, lw, dw = tiny
+    m = wl.moe
+    dev = torch.device("cuda:0")
+    ws = ops.workspace(ops.moe_workspace_bytes(1, m.H, m.I, m.E, m.k), dev)
+    get = lambda e: (lw["w13c"][e], lw["w13s"][e], lw["w2c"][e], lw["w2s"][e])
+    cases = (([3, 11], [0.75, 0.25]), ([5], [1.0]), ([], []), ([2, 99], [0.625, 0.375]), ([0, 15], [0.5, 0.5]))
+    for i, (ids, wts) in enumerate(cases * 2):
+        shared = dw["shared"] if i % 3 != 1 else None
+        x = inputs.normal_bf16((3, 2, i), (1, m.H), 1.0)
+        res = inputs.normal_bf16((3, 3, i), (1, m.H), 1.0)
+        el_dev = np.zeros(1 + m.k, dtype=np.int32)
+        el_dev[0] = len(ids)
+        el_dev[1:1 + len(ids)] = ids
+        sw_dev = np.zeros((m.k, 1), dtype=np.float32)
+        sw_dev[:len(ids), 0] = wts
+        args = (P.to_dev_bf16(x), dw["w13c"], dw["w13s"], dw["w2c"], dw["w2s"], P.to_dev(el_dev), P.to_dev(sw_dev),
+                m.k)
+        y, h = ops.moe_expert_gemv_mxfp4(*args, shared=shared, residual=P.to_dev_bf16(res), ws=ws)
+        y1, h1 = ops.moe_expert_gemv_mxfp4(*args, shared=shared, residual=P.to_dev_bf16(res))
+        y, h, y1, h1 = P.np_(y), P.bits(h), P.np_(y1), P.bits(h1)
+        assert np.array_equal(y, y1) and np.array_equal(h, h1), (i, ids)
+        valid = [(e, wt) for e, wt in zip(ids, wts) if 0 <= e < m.E]
+        d = [OM.down(OM.gate_up(x, *get(e)[:2], m.I), *get(e)[2:]) for e, _ in valid]
+        d = np.stack(d) if d else np.zeros((0, 1, m.H))
+        sw_ref = np.array([[wt] for _, wt in valid]).reshape(len(valid), 1)
+        sh = lw["shared"]
+        d_sh = OM.down(OM.gate_up(x, sh[0], sh[1], m.I), sh[2], sh[3]) if shared is not None else None
+        y_ref = OM.combine(d, sw_ref, d_sh)
+        if not valid and shared is None:
+            assert np.array_equal(y, np.zeros_like(y)), (i, ids)
+        else:
+            ok, worst = C.fp_close(y, y_ref)
+            assert ok, (i, ids, worst)
+        P.check_residual(res, y, h)
+
+
 def test_router_ties_resolve_to_lowest_id(ops):
     H, E, k = 256, 64, 8
     w = inputs.normal_f32((4,), (E, H), 0.02)
@@ -213,10 +254,11 @@ def test_identical_tokens_give_identical_rows(ops, ling):
     assert C.fp_close(y1, y[:1])[0]
 
 
-def test_layer_is_deterministic(ops, ling):
+@pytest.mark.parametrize("T", [1, 4])
+def test_layer_is_deterministic(ops, ling, T):
     wl, lw, dw = ling
-    x = inputs.normal_bf16((31,), (4, wl.moe.H), 1.0)
-    res = inputs.normal_bf16((32,), (4, wl.moe.H), 1.0)
+    x = inputs.normal_bf16((31, T), (T, wl.moe.H), 1.0)
+    res = inputs.normal_bf16((32, T), (T, wl.moe.H), 1.0)
     first = run_layer(ops, wl, dw, x, res)
     for _ in range(10):
         again = run_layer(ops, wl, dw, x, res)

@@ -732,7 +732,7 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ lrow, int E
   const int e0 = P * t;
   float v[P];
 #pragma unroll
-  for (int i = 0; i < P; ++i) v[i] = (e0 + i < E) ? ld_dev(lrow + e0 + i) : -INFINITY;
+  for (int i = 0; i < P; ++i) v[i] = (e0 + i < E) ? __uint_as_float(ld_coh4(lrow, (uint32_t)(e0 + i) * 4)) : -INFINITY;
   float bv = v[0];
   int bi = e0;
 #pragma unroll
@@ -786,64 +786,86 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ lrow, int E
   __syncthreads();
 }
 
-// Top-k of one token's E logits (E <= 64 PW, k <= 8) by one wavefront, in
-// registers.  Lane l holds logits PW l .. PW l + PW - 1 as 64-bit rank keys
-// (order-preserving value bits over the complemented id, so one unsigned
-// compare orders by value, then lower id; positions past E get key 0).  A
-// logit beaten by the maxima of k other lanes is beaten by k logits, so the
-// top k lie in the k lanes whose maxima rank highest.  Those lanes' keys go
-// to this wavefront's LDS slots (rank-major, zeros elsewhere), and each of the
-// 8 PW candidates is ranked against the others through readlane broadcasts.
-// Leaves the k (logit, id) pairs in rank order in rv / rid.
+// Top-k of one token's E logits (E <= 64 PW, k <= 8) by one wavefront.  Lane
+// l holds logits PW l .. PW l + PW - 1 as 64-bit rank keys (order-preserving
+// value bits over the complemented id, so one unsigned compare orders by
+// value, then lower id; positions past E get key 0).  A logit beaten by the
+// maxima of k other lanes is beaten by k logits, so the top k lie in the k
+// lanes whose maxima rank highest.  Each lane's maximum is ranked by counting
+// the larger ones among all 64, read back from this wavefront's LDS scratch
+// (every lane reads the same words, so the reads are broadcasts); the keys of
+// the k best lanes go to the candidate slots (rank-major, zeros elsewhere),
+// and each of the 8 PW candidates is ranked the same way.  Leaves the k
+// (logit, id) pairs in rank order in rv / rid.  scratch: 64 + 8 PW keys,
+// 16-byte aligned, used by this wavefront alone.
+//
+// The logits were stored by other workgroups of the launch: they are read with
+// device-coherent buffer loads, which (unlike atomic loads) the compiler
+// issues together, so a wavefront pays one round trip for all of them.
+template <int PW>
+__device__ __forceinline__ void wave_load_logits(const float* logits, size_t row0, int E, float (&v)[PW]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const int e = PW * lane + i;
+    v[i] = e < E ? __uint_as_float(ld_coh4(logits, (uint32_t)(row0 + e) * 4)) : 0.f;
+  }
+}
 
 template <int PW>
-__device__ __forceinline__ void wave_topk(const float* __restrict__ lrow, int E, int k, RankKey* cand, float* rv,
-                                          int* rid) {
+__device__ __forceinline__ void wave_topk_values(const float (&v)[PW], int E, int k, RankKey* scratch, float* rv,
+                                                 int* rid) {
   constexpr int NC = 8 * PW;                  // candidate slots: 8 lanes x PW
   constexpr int CPL = (NC + 63) / 64;         // candidates per lane
+  RankKey* mxs = scratch;                     // [64] lane maxima
+  RankKey* cand = scratch + 64;               // [NC]
   const int lane = threadIdx.x & 63;
   RankKey key[PW];
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
     const int e = PW * lane + i;
-    key[i] = e < E ? rank_key(ld_dev(lrow + e), e) : 0ull;
+    key[i] = e < E ? rank_key(v[i], e) : 0ull;
   }
   RankKey mx = key[0];
 #pragma unroll
   for (int i = 1; i < PW; ++i) mx = key[i] > mx ? key[i] : mx;
-  int r = 0;
-#pragma unroll
-  for (int j = 0; j < 64; ++j) r += (int)(readlane_key(mx, j) > mx);
+  mxs[lane] = mx;
 #pragma unroll
   for (int m = 0; m < CPL; ++m)
     if (lane + 64 * m < NC) cand[lane + 64 * m] = 0ull;
+  // LDS accesses of one wavefront complete in order: only the compiler has to
+  // keep these stores before the reads below
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int r = count_greater(mxs, 0, 64, mx);
   if (r < k) {
 #pragma unroll
     for (int i = 0; i < PW; ++i) cand[r * PW + i] = key[i];
   }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  RankKey cv[CPL];
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-  for (int m = 0; m < CPL; ++m) cv[m] = lane + 64 * m < NC ? cand[lane + 64 * m] : 0ull;
-  int rk[CPL];
-#pragma unroll
-  for (int m = 0; m < CPL; ++m) rk[m] = 0;
-#pragma unroll
-  for (int m2 = 0; m2 < CPL; ++m2)
-#pragma unroll
-    for (int j = 0; j < 64; ++j) {
-      const RankKey o = readlane_key(cv[m2], j);
-#pragma unroll
-      for (int m = 0; m < CPL; ++m) rk[m] += (int)(o > cv[m]);
+  for (int m = 0; m < CPL; ++m) {
+    const RankKey cv = lane + 64 * m < NC ? cand[lane + 64 * m] : 0ull;
+    const int rk = count_greater(cand, 0, NC, cv);
+    if (cv != 0ull && rk < k) {
+      rv[rk] = key_value(cv);
+      rid[rk] = key_id(cv);
     }
-#pragma unroll
-  for (int m = 0; m < CPL; ++m)
-    if (cv[m] != 0ull && rk[m] < k) {
-      rv[rk[m]] = key_value(cv[m]);
-      rid[rk[m]] = key_id(cv[m]);
-    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int PW>
+__device__ __forceinline__ void wave_topk(const float* logits, size_t row0, int E, int k, RankKey* scratch, float* rv,
+                                          int* rid) {
+  float v[PW];
+  wave_load_logits<PW>(logits, row0, E, v);
+  wave_topk_values<PW>(v, E, k, scratch, rv, rid);
 }
 
 // Router GEMV with one row per wavefront (64 lanes; lane l takes the 16-byte
@@ -913,7 +935,7 @@ __global__ void __launch_bounds__(256) router_topk_kernel(
   // in rank order, per token; one token takes the whole workgroup, several
   // take one wavefront each, side by side
   __shared__ TopkScratch R;
-  __shared__ RankKey wcand[WSX_MAX_T][8 * 4 * P];
+  __shared__ __attribute__((aligned(16))) RankKey wcand[WSX_MAX_T][64 + 8 * 4 * P];
   __shared__ float wrv[WSX_MAX_T][WSX_MAX_K];
   __shared__ int wrid[WSX_MAX_T][WSX_MAX_K];
   __shared__ int sel_id[WSX_MAX_T * WSX_MAX_K];
@@ -930,7 +952,7 @@ __global__ void __launch_bounds__(256) router_topk_kernel(
   } else {
     t = wave;
     if (wave < T) {
-      wave_topk<4 * P>(logits + (size_t)t * E, E, k, wcand[t], wrv[t], wrid[t]);
+      wave_topk<4 * P>(logits, (size_t)t * E, E, k, wcand[t], wrv[t], wrid[t]);
       if (lane < k) j0 = lane;
     }
     rv_t = wrv[t < T ? t : 0];
@@ -985,13 +1007,36 @@ __global__ void __launch_bounds__(256) router_topk_kernel(
 // The router of a small batch or a longer draft (5 <= T <= WSX_MAX_T_MOE
 // tokens; [saipien] "Draft three tokens, verify four" for the verify pass
 // this generalizes).  The GEMV is the one above with the tokens staged in LDS
-// four at a time (their rows stay in registers across the chunks), so the
-// stage never exceeds 4 K bf16.  The last workgroup ranks each token on one
-// wavefront (wavefront w takes tokens w, w + 4, ...), then builds the compact
-// list from the T k selections with the whole workgroup: selection j keeps
-// its id if no earlier selection has it, and every selection's slot is the
-// number of distinct smaller ids.
+// four at a time (their rows stay in registers across the stages), so the
+// stage never exceeds 4 K bf16.  Each thread issues all of a stage's loads at
+// once; for rows of up to 5 granules per lane every stage is requested before
+// the first is stored, for up to 10 the next stage's loads are in flight while
+// the current one is multiplied.  The last workgroup ranks
+// each token on one wavefront (wavefront w takes tokens w, w + 4, ..., and
+// reads all of their logits at once), then builds the compact list from the
+// T k selections through a bitmap of the selected ids: an id's slot is the
+// number of selected ids below it.
 constexpr int kRouteChunk = 4;
+
+// Load / store one stage of up to kRouteChunk tokens (nx 16-byte chunks per
+// token) with XPC chunks per thread, every load issued before the first use.
+template <int XPC>
+__device__ __forceinline__ void route_stage_load(const uint16_t* x, int tc, int nt, int nx, uint4 (&r)[XPC]) {
+  const uint4* src = reinterpret_cast<const uint4*>(x) + (size_t)tc * nx;
+#pragma unroll
+  for (int i = 0; i < XPC; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    r[i] = c < nt * nx ? src[c] : make_uint4(0, 0, 0, 0);
+  }
+}
+template <int XPC>
+__device__ __forceinline__ void route_stage_store(const uint4 (&r)[XPC], int nt, int nx, uint16_t* xs) {
+#pragma unroll
+  for (int i = 0; i < XPC; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    if (c < nt * nx) reinterpret_cast<uint4*>(xs)[c] = r[i];
+  }
+}
 
 template <int WT, int RGPL, int P>
 __global__ void __launch_bounds__(256) router_topk_grouped_kernel(
@@ -999,10 +1044,18 @@ __global__ void __launch_bounds__(256) router_topk_grouped_kernel(
     int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, int32_t* __restrict__ expert_list,
     float* __restrict__ slot_w, unsigned* counter) {
   constexpr int DW = WTraits<WT>::EPG / 2;
-  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [kRouteChunk][K]
+  // 16-byte chunks of one stage per thread: kRouteChunk K / 8 / 256 <= RGPL
+  // for both weight types (RGPL = ceil(K / EPG / 64))
+  constexpr int XPC = RGPL;
+  constexpr bool kAllStages = RGPL <= 5;   // all stages in registers (4 XPC chunks per thread)
+  constexpr bool kPrefetch = RGPL <= 10;   // else the next stage in flight during the dots
+  // [kRouteChunk][K] bf16 stages; in the last workgroup's tail, the [T][E] logits
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
   __shared__ int flag;
+  __shared__ float lg[WSX_MAX_T_MOE][4];   // this workgroup's logits, stored once after the stages
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int G = K / WTraits<WT>::EPG;
+  const int nx = K / 8;
   const size_t row_bytes = (size_t)K * WTraits<WT>::ESZ;
   const uint32_t* xs32 = reinterpret_cast<const uint32_t*>(xs);
   for (int r0 = blockIdx.x * 4; r0 < E; r0 += gridDim.x * 4) {   // uniform across the workgroup
@@ -1014,44 +1067,122 @@ __global__ void __launch_bounds__(256) router_topk_grouped_kernel(
       const int g = lane + 64 * j;
       wv[j] = (ok && g < G) ? ld16(W + (size_t)row * row_bytes + (size_t)g * 16) : make_uint4(0, 0, 0, 0);
     }
-    for (int tc = 0; tc < T; tc += kRouteChunk) {
-      const int nt = T - tc < kRouteChunk ? T - tc : kRouteChunk;
-      __syncthreads();   // the previous chunk's reads are done
-      const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)tc * K);
-      uint4* dst = reinterpret_cast<uint4*>(xs);
-      for (int c = threadIdx.x; c < nt * K / 8; c += 256) dst[c] = src[c];
-      __syncthreads();
-      if (ok) {
-        for (int t = 0; t < nt; ++t) {
-          float acc = 0.f;
+    // the logits of the staged tokens tc .. tc + nt - 1 for this wavefront's row
+    auto dots = [&](int tc, int nt) {
+      if (!ok) return;
+      for (int t = 0; t < nt; ++t) {
+        float acc = 0.f;
 #pragma unroll
-          for (int j = 0; j < RGPL; ++j) {
-            const int g = lane + 64 * j;
-            if (g < G) {
-              uint32_t xp[DW];
+        for (int j = 0; j < RGPL; ++j) {
+          const int g = lane + 64 * j;
+          if (g < G) {
+            uint32_t xp[DW];
 #pragma unroll
-              for (int d = 0; d < DW; ++d) xp[d] = xs32[(size_t)t * (K / 2) + (size_t)g * DW + d];
-              acc += granule_dot<WT>(wv[j], xp);
-            }
+            for (int d = 0; d < DW; ++d) xp[d] = xs32[(size_t)t * (K / 2) + (size_t)g * DW + d];
+            acc += granule_dot<WT>(wv[j], xp);
           }
-          const float sres = wave_sum_dpp(acc);
-          if (lane == 0) st_dev(logits + (size_t)(tc + t) * E + row, sres);
         }
+        const float sres = wave_sum_dpp(acc);
+        if (lane == 0) lg[tc + t][wave] = sres;
       }
+    };
+    if constexpr (kAllStages) {
+      // every stage requested at once: one memory latency for all of them
+      constexpr int NS = WSX_MAX_T_MOE / kRouteChunk;
+      uint4 xall[NS][XPC];
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const int nt = T - st * kRouteChunk;
+        route_stage_load<XPC>(x, st * kRouteChunk, nt < 0 ? 0 : (nt > kRouteChunk ? kRouteChunk : nt), nx, xall[st]);
+      }
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const int tc = st * kRouteChunk;
+        if (tc >= T) break;
+        const int nt = T - tc < kRouteChunk ? T - tc : kRouteChunk;
+        lds_barrier();   // the previous stage's LDS reads are done
+        route_stage_store<XPC>(xall[st], nt, nx, xs);
+        lds_barrier();
+        dots(tc, nt);
+      }
+    } else {
+      uint4 xa[XPC];
+      route_stage_load<XPC>(x, 0, T < kRouteChunk ? T : kRouteChunk, nx, xa);
+      for (int tc = 0; tc < T; tc += kRouteChunk) {
+        const int nt = T - tc < kRouteChunk ? T - tc : kRouteChunk;
+        lds_barrier();   // the previous stage's LDS reads are done
+        route_stage_store<XPC>(xa, nt, nx, xs);
+        const int tn = tc + kRouteChunk;
+        const int ntn = T - tn < kRouteChunk ? T - tn : kRouteChunk;
+        if (kPrefetch && tn < T) route_stage_load<XPC>(x, tn, ntn, nx, xa);   // in flight during the dots
+        lds_barrier();
+        dots(tc, nt);
+        if (!kPrefetch && tn < T) route_stage_load<XPC>(x, tn, ntn, nx, xa);
+      }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < T * 4; i += 256) {
+      const int t = i >> 2, rr = r0 + (i & 3);
+      if (rr < E) st_dev(logits + (size_t)t * E + rr, lg[t][i & 3]);
     }
   }
   if (!last_block_arrived(counter, gridDim.x, &flag)) return;
 
   // ---- last workgroup: per token, top-k and softmax in rank order
-  __shared__ RankKey wcand[4][8 * 4 * P];
+  constexpr int PW = 4 * P;
+  __shared__ __attribute__((aligned(16))) RankKey wcand[4][64 + 8 * PW];
   __shared__ float wrv[4][WSX_MAX_K];
   __shared__ int wrid[4][WSX_MAX_K];
   __shared__ int sel_id[WSX_MAX_T_MOE * WSX_MAX_K];
   __shared__ float sel_w[WSX_MAX_T_MOE * WSX_MAX_K];
-  __shared__ int first[WSX_MAX_T_MOE * WSX_MAX_K];
   __shared__ float sw_tab[WSX_MAX_T_MOE * WSX_MAX_K * WSX_MAX_T_MOE];
-  for (int t = wave; t < T; t += 4) {
-    wave_topk<4 * P>(logits + (size_t)t * E, E, k, wcand[wave], wrv[wave], wrid[wave]);
+  __shared__ unsigned bm[WSX_MAX_E / 32];   // bitmap of the selected ids
+  __shared__ int wpre[WSX_MAX_E / 32];      // selected ids below each bitmap word
+  // every logit of the layer into LDS (the stage area is free now), with all
+  // of a thread's loads in flight together
+  float* ls = reinterpret_cast<float*>(xs);
+  {
+    const int nl = T * E;
+    if ((nl & 3) == 0) {
+      constexpr int CPT = WSX_MAX_T_MOE * WSX_MAX_E / 4 / 256;   // 16-byte loads per thread at most
+      uint4 v[CPT];
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        const int i = threadIdx.x + 256 * j;
+        v[j] = i < nl / 4 ? ld_coh16(logits, (uint32_t)i * 16) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        const int i = threadIdx.x + 256 * j;
+        if (i < nl / 4) reinterpret_cast<uint4*>(ls)[i] = v[j];
+      }
+    } else {
+      for (int i0 = 0; i0 < nl; i0 += 256 * 16) {
+        uint32_t v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int i = i0 + threadIdx.x + 256 * j;
+          v[j] = i < nl ? ld_coh4(logits, (uint32_t)i * 4) : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int i = i0 + threadIdx.x + 256 * j;
+          if (i < nl) ls[i] = __uint_as_float(v[j]);
+        }
+      }
+    }
+  }
+  const int n = T * k;
+  const int nw = (E + 31) / 32;
+  for (int e = threadIdx.x; e < n * T; e += 256) sw_tab[e] = 0.f;
+  if (threadIdx.x < nw) bm[threadIdx.x] = 0u;
+  __syncthreads();
+#pragma unroll 1
+  for (int t = wave; t < T; t += 4) {   // uniform across the wavefront
+    float lv[PW];
+#pragma unroll
+    for (int i = 0; i < PW; ++i) lv[i] = PW * lane + i < E ? ls[(size_t)t * E + PW * lane + i] : 0.f;
+    wave_topk_values<PW>(lv, E, k, wcand[wave], wrv[wave], wrid[wave]);
     if (lane < k) {
       const float top = wrv[wave][0];
       float zs = 0.f, mine = 0.f;
@@ -1076,27 +1207,31 @@ __global__ void __launch_bounds__(256) router_topk_grouped_kernel(
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
-  const int n = T * k;
-  for (int e = threadIdx.x; e < n * T; e += 256) sw_tab[e] = 0.f;
   __syncthreads();
   for (int j = threadIdx.x; j < n; j += 256) {
     const int id = sel_id[j];
-    int f = 1;
-    for (int i = 0; i < j; ++i) f &= (sel_id[i] != id);
-    first[j] = f;
+    atomicOr(&bm[id >> 5], 1u << (id & 31));
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // exclusive prefix of the words' popcounts (nw <= 32 lanes)
+    const int c = lane < nw ? __popc(bm[lane]) : 0;
+    int incl = c;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d);
+      if (lane >= d) incl += o;
+    }
+    if (lane < nw) wpre[lane] = incl - c;
+    if (lane == 63) expert_list[0] = incl;
   }
   __syncthreads();
   for (int j = threadIdx.x; j < n; j += 256) {
     const int id = sel_id[j];
-    int rank = 0;
-    for (int i = 0; i < n; ++i) rank += first[i] & (sel_id[i] < id);
-    if (first[j]) expert_list[1 + rank] = id;
+    const int w = id >> 5;
+    const int rank = wpre[w] + __popc(bm[w] & ((1u << (id & 31)) - 1u));
+    expert_list[1 + rank] = id;   // every selection of an id writes the same value
     sw_tab[rank * T + j / k] = sel_w[j];   // a token's k ids are distinct: one entry per (slot, token)
-  }
-  if (threadIdx.x == 0) {
-    int tot = 0;
-    for (int i = 0; i < n; ++i) tot += first[i];
-    expert_list[0] = tot;
   }
   __syncthreads();
   for (int e = threadIdx.x; e < n * T; e += 256) slot_w[e] = sw_tab[e];
@@ -1309,7 +1444,8 @@ static hipError_t launch_router_grouped(const void* W, int E, int K, int k, cons
   const int G = K / WTraits<WT>::EPG;
   const int rgpl = (G + 63) / 64;
   const int grid = (E + 3) / 4;
-  const size_t lds = (size_t)kRouteChunk * K * 2;
+  // the stages, and then the [T][E] logits in the last workgroup's tail
+  const size_t lds = (size_t)kRouteChunk * K * 2 > (size_t)T * E * 4 ? (size_t)kRouteChunk * K * 2 : (size_t)T * E * 4;
   const bool small = E <= 512;
 #define WSX_RG_CASE(N)                                                                                            \
   case N:                                                                                                         \
