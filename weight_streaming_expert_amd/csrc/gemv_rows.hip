@@ -812,6 +812,23 @@ __device__ __forceinline__ void wave_load_logits(const float* logits, size_t row
   }
 }
 
+// Number of the N keys at buf (16-byte aligned) greater than m, with the LDS
+// reads issued 32 keys at a time, so a count pays N / 32 LDS latencies.
+template <int N>
+__device__ __forceinline__ int count_greater_n(const RankKey* buf, RankKey m) {
+  static_assert(N % 32 == 0, "whole batches");
+  int r = 0;
+#pragma unroll
+  for (int j0 = 0; j0 < N; j0 += 32) {
+    ulonglong2 p[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) p[j] = reinterpret_cast<const ulonglong2*>(buf + j0)[j];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) r += (int)(p[j].x > m) + (int)(p[j].y > m);
+  }
+  return r;
+}
+
 template <int PW>
 __device__ __forceinline__ void wave_topk_values(const float (&v)[PW], int E, int k, RankKey* scratch, float* rv,
                                                  int* rid) {
@@ -838,7 +855,7 @@ __device__ __forceinline__ void wave_topk_values(const float (&v)[PW], int E, in
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const int r = count_greater(mxs, 0, 64, mx);
+  const int r = count_greater_n<64>(mxs, mx);
   if (r < k) {
 #pragma unroll
     for (int i = 0; i < PW; ++i) cand[r * PW + i] = key[i];
@@ -849,7 +866,7 @@ __device__ __forceinline__ void wave_topk_values(const float (&v)[PW], int E, in
 #pragma unroll
   for (int m = 0; m < CPL; ++m) {
     const RankKey cv = lane + 64 * m < NC ? cand[lane + 64 * m] : 0ull;
-    const int rk = count_greater(cand, 0, NC, cv);
+    const int rk = count_greater_n<NC>(cand, cv);
     if (cv != 0ull && rk < k) {
       rv[rk] = key_value(cv);
       rid[rk] = key_id(cv);
@@ -866,6 +883,22 @@ __device__ __forceinline__ void wave_topk(const float* logits, size_t row0, int 
   float v[PW];
   wave_load_logits<PW>(logits, row0, E, v);
   wave_topk_values<PW>(v, E, k, scratch, rv, rid);
+}
+
+// DW consecutive dwords from LDS as one vector read (the address is a multiple
+// of 4 DW bytes).
+template <int DW>
+__device__ __forceinline__ void lds_dwords(const uint32_t* p, uint32_t (&d)[DW]) {
+  if constexpr (DW == 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+  } else if constexpr (DW == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    d[0] = v.x; d[1] = v.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < DW; ++i) d[i] = p[i];
+  }
 }
 
 // Router GEMV with one row per wavefront (64 lanes; lane l takes the 16-byte
@@ -901,19 +934,16 @@ __global__ void __launch_bounds__(256) router_topk_kernel(
     float acc[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[t] = 0.f;
+    // granules past the row end hold zero weights: their reads (clamped into
+    // the row) add nothing, and each token still sums its granules in order
 #pragma unroll
     for (int j = 0; j < RGPL; ++j) {
-      const int g = lane + 64 * j;
-      if (g < G) {
+      const int g = min(lane + 64 * j, G - 1);
+      uint32_t xp[T][DW];
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-          uint32_t xp[DW];
-          const uint32_t* src = xs32 + (size_t)t * (K / 2) + (size_t)g * DW;
+      for (int t = 0; t < T; ++t) lds_dwords<DW>(xs32 + (size_t)t * (K / 2) + (size_t)g * DW, xp[t]);
 #pragma unroll
-          for (int d = 0; d < DW; ++d) xp[d] = src[d];
-          acc[t] += granule_dot<WT>(wv[j], xp);
-        }
-      }
+      for (int t = 0; t < T; ++t) acc[t] += granule_dot<WT>(wv[j], xp[t]);
     }
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -1018,6 +1048,7 @@ __global__ void __launch_bounds__(256) router_topk_kernel(
 // number of selected ids below it.
 constexpr int kRouteChunk = 4;
 
+
 // Load / store one stage of up to kRouteChunk tokens (nx 16-byte chunks per
 // token) with XPC chunks per thread, every load issued before the first use.
 template <int XPC>
@@ -1067,23 +1098,44 @@ __global__ void __launch_bounds__(256) router_topk_grouped_kernel(
       const int g = lane + 64 * j;
       wv[j] = (ok && g < G) ? ld16(W + (size_t)row * row_bytes + (size_t)g * 16) : make_uint4(0, 0, 0, 0);
     }
-    // the logits of the staged tokens tc .. tc + nt - 1 for this wavefront's row
+    // the logits of the staged tokens tc .. tc + nt - 1 for this wavefront's
+    // row: the four token slots side by side, each granule's activations read
+    // for all of them before the products (slots past nt are computed and
+    // dropped).  Granules past the row end hold zero weights, so their reads
+    // (clamped into the row) add nothing; each token still sums its granules
+    // in order.
     auto dots = [&](int tc, int nt) {
       if (!ok) return;
-      for (int t = 0; t < nt; ++t) {
-        float acc = 0.f;
+      if constexpr (RGPL > 16) {   // long rows: one token at a time keeps the registers in bounds
+        for (int t = 0; t < nt; ++t) {
+          float a = 0.f;
 #pragma unroll
-        for (int j = 0; j < RGPL; ++j) {
-          const int g = lane + 64 * j;
-          if (g < G) {
+          for (int j = 0; j < RGPL; ++j) {
             uint32_t xp[DW];
-#pragma unroll
-            for (int d = 0; d < DW; ++d) xp[d] = xs32[(size_t)t * (K / 2) + (size_t)g * DW + d];
-            acc += granule_dot<WT>(wv[j], xp);
+            lds_dwords<DW>(xs32 + (size_t)t * (K / 2) + (size_t)min(lane + 64 * j, G - 1) * DW, xp);
+            a += granule_dot<WT>(wv[j], xp);
           }
+          const float sres = wave_sum_dpp(a);
+          if (lane == 0) lg[tc + t][wave] = sres;
         }
-        const float sres = wave_sum_dpp(acc);
-        if (lane == 0) lg[tc + t][wave] = sres;
+        return;
+      }
+      float acc[kRouteChunk];
+#pragma unroll
+      for (int t = 0; t < kRouteChunk; ++t) acc[t] = 0.f;
+#pragma unroll
+      for (int j = 0; j < RGPL; ++j) {
+        const int g = min(lane + 64 * j, G - 1);
+        uint32_t xp[kRouteChunk][DW];
+#pragma unroll
+        for (int t = 0; t < kRouteChunk; ++t) lds_dwords<DW>(xs32 + (size_t)t * (K / 2) + (size_t)g * DW, xp[t]);
+#pragma unroll
+        for (int t = 0; t < kRouteChunk; ++t) acc[t] += granule_dot<WT>(wv[j], xp[t]);
+      }
+#pragma unroll
+      for (int t = 0; t < kRouteChunk; ++t) {
+        const float sres = wave_sum_dpp(acc[t]);
+        if (t < nt && lane == 0) lg[tc + t][wave] = sres;
       }
     };
     if constexpr (kAllStages) {
