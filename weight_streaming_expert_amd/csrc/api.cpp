@@ -39,7 +39,8 @@ MoeWs moe_ws(int T, int H, int I, int E, int k) {
   w.logits = align256(w.dcnt + (size_t)(H / 32 + 1) * 64);
   w.a = align256(w.logits + (size_t)T * E * 4);
   w.part = align256(w.a + (size_t)(T * k + 1) * T * I * 4);
-  w.total = align256(w.part + (size_t)down_groups(T * k + 1) * T * H * 4);
+  const int ng = down_groups(T * k + 1) > down_sparse_groups(T, k) ? down_groups(T * k + 1) : down_sparse_groups(T, k);
+  w.total = align256(w.part + (size_t)ng * T * H * 4);
   return w;
 }
 size_t head_ws_bytes() { return 256 + (size_t)2 * kHeadMaxGrid * WSX_MAX_T * 4; }

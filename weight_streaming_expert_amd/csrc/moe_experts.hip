@@ -802,9 +802,23 @@ __global__ void __launch_bounds__(256) moe_down_grouped_kernel(
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[r][t] = 0.f;
+  // routed slot s < n_active, or part v = s - n_active of the shared expert
+  // (tokens 4 v .. 4 v + 3), whose activations sit in slot n_active
+  const bool shared_part = has_sh && s >= n_active && s - n_active < (T + 3) / 4;
   const uint8_t *C = nullptr, *S = nullptr;
-  const bool active = s < nslots && slot_expert_pre(s, n_active, has_sh, E, e_slot, w2c, w2s, sh2c, sh2s,
-                                                    (size_t)H * (I / 2), (size_t)H * (I / 32), &C, &S);
+  bool active = false;
+  if (s < n_active) {
+    active = e_slot >= 0 && e_slot < E;
+    if (active) {
+      C = w2c + (size_t)e_slot * ((size_t)H * (I / 2));
+      S = w2s + (size_t)e_slot * ((size_t)H * (I / 32));
+    }
+  } else if (shared_part) {
+    active = true;
+    C = sh2c;
+    S = sh2s;
+  }
+  const int as_slot = s < n_active ? s : n_active;
   if (active) {
     // weights first (their latency overlaps the staging)
     const size_t rowc = I / 2, rows = I / 32;
@@ -913,15 +927,21 @@ __global__ void __launch_bounds__(256) moe_down_grouped_kernel(
 
 // Down + weighted combine + residual for 5..16 tokens, over expert-sorted
 // token lists: the slots are the active experts in ascending id order, and
-// slot s's tokens are those with a nonzero weight slot_w[s][t] (all tokens for
-// the shared expert).  Workgroup (tile, g) owns rows n0 .. n0+31 and the
-// slots 4g .. 4g+3, one per wavefront, as in the grouped kernel above; a
-// wavefront takes its slot's tokens four at a time, staging their activations
-// in LDS and forming the 32 rows x 4 tokens of partial sums from the same
-// decoded weights, so the work follows the routed (slot, token) pairs, not
-// slots x T.  Each slot's weighted contribution per (token, row) lands in LDS,
-// the four wavefronts are added in slot order, and the groups are added in
-// group order by the tile's last workgroup.
+// slot s's tokens are those with a nonzero weight slot_w[s][t].  The shared
+// expert, which serves every token, is split into ceil(T / 4) work slots of
+// four tokens each (after the routed slots), so no wavefront carries all T
+// tokens.  Workgroup (tile, g) owns rows n0 .. n0+31 and the work slots
+// 4g .. 4g+3, one per wavefront, as in the grouped kernel above; a wavefront
+// takes its slot's tokens two at a time, staging their activations in LDS and
+// forming the 32 rows x 2 tokens of partial sums from the same decoded
+// weights, so the work follows the routed (slot, token) pairs, not slots x T.
+// Two tokens per pass keep the registers and the LDS stage small enough for
+// three workgroups per CU (at most two passes per work slot).  Each slot's
+// weighted contribution per (token, row) lands in LDS, the four wavefronts
+// are added in slot order, and the groups
+// are added in group order by the tile's last workgroup.
+int down_sparse_groups(int T, int k) { return (T * k + (T + 3) / 4 + 3) / 4; }
+
 template <int NKB>
 __global__ void __launch_bounds__(256) moe_down_sparse_kernel(
     int T, int H, int I, int E, int max_slots, const uint8_t* __restrict__ w2c, const uint8_t* __restrict__ w2s,
@@ -929,13 +949,12 @@ __global__ void __launch_bounds__(256) moe_down_sparse_kernel(
     const float* __restrict__ slot_w, const float* __restrict__ a_in, const uint16_t* __restrict__ residual,
     float* __restrict__ out_y, uint16_t* __restrict__ out_h, uint16_t* __restrict__ out_h2, float* part,
     unsigned* counters) {
-  constexpr int TC = 4;   // tokens per pass
-  const int s = 4 * (int)blockIdx.y + (int)(threadIdx.x >> 6);
+  constexpr int TC = 2;   // tokens per pass
+  const int s = 4 * (int)blockIdx.y + (int)(threadIdx.x >> 6);   // work slot
   int n_active = expert_list[0];
   const int e_slot = s < max_slots - 1 ? expert_list[1 + s] : -1;
   n_active = n_active < 0 ? 0 : (n_active > max_slots - 1 ? max_slots - 1 : n_active);
   const bool has_sh = sh2c != nullptr;
-  const int nslots = n_active + (has_sh ? 1 : 0);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kg = lane & 7, rq = lane >> 3;
   const int n0 = blockIdx.x * kDnRows;
@@ -947,26 +966,42 @@ __global__ void __launch_bounds__(256) moe_down_sparse_kernel(
   __shared__ int flag;
   float* aw = as + (size_t)wave * TC * lstride;
   for (int i = lane; i < WSX_MAX_T_MOE * kDnRows; i += 64) yw[wave][i / kDnRows][i % kDnRows] = 0.f;
+  // routed slot s < n_active, or part v = s - n_active of the shared expert
+  // (tokens 4 v .. 4 v + 3), whose activations sit in slot n_active
+  const bool shared_part = has_sh && s >= n_active && s - n_active < (T + 3) / 4;
   const uint8_t *C = nullptr, *S = nullptr;
-  const bool active = s < nslots && slot_expert_pre(s, n_active, has_sh, E, e_slot, w2c, w2s, sh2c, sh2s,
-                                                    (size_t)H * (I / 2), (size_t)H * (I / 32), &C, &S);
+  bool active = false;
+  if (s < n_active) {
+    active = e_slot >= 0 && e_slot < E;
+    if (active) {
+      C = w2c + (size_t)e_slot * ((size_t)H * (I / 2));
+      S = w2s + (size_t)e_slot * ((size_t)H * (I / 32));
+    }
+  } else if (shared_part) {
+    active = true;
+    C = sh2c;
+    S = sh2s;
+  }
+  const int as_slot = s < n_active ? s : n_active;
   if (active) {
     const size_t rowc = I / 2, rows = I / 32;
     uint4 cw[NKB][4];
-    float sc[NKB][4];
+    uint32_t sb[NKB];   // the four rows' E8M0 scale bytes, row r in byte r
 #pragma unroll
     for (int b = 0; b < NKB; ++b) {
       const int kb = kg + 8 * b;
+      sb[b] = 0u;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = n0 + 4 * rq + r;
         cw[b][r] = kb < NB ? ld16(C + row * rowc + (size_t)kb * 16) : make_uint4(0, 0, 0, 0);
-        sc[b][r] = kb < NB ? e8m0_to_f32(S[row * rows + kb]) : 0.f;
+        sb[b] |= (kb < NB ? (uint32_t)S[row * rows + kb] : 0u) << (8 * r);
       }
     }
     // the slot's token list: lane t < T holds token t's weight
+    const int v4 = 4 * (s - n_active);
     const float wl = lane < T ? (s < n_active ? slot_w[s * T + lane] : 1.0f) : 0.f;
-    unsigned long long tm = __ballot(lane < T && wl != 0.f);
+    unsigned long long tm = s < n_active ? __ballot(lane < T && wl != 0.f) : __ballot(lane >= v4 && lane < v4 + 4 && lane < T);
     while (tm) {
       int tok[TC];
       float wt[TC];
@@ -982,7 +1017,8 @@ __global__ void __launch_bounds__(256) moe_down_sparse_kernel(
       float4 av4[TC][NKB];
 #pragma unroll
       for (int j = 0; j < TC; ++j) {
-        const float4* src = reinterpret_cast<const float4*>(a_in + ((size_t)s * T + (tok[j] < 0 ? 0 : tok[j])) * I);
+        const float4* src =
+            reinterpret_cast<const float4*>(a_in + ((size_t)as_slot * T + (tok[j] < 0 ? 0 : tok[j])) * I);
 #pragma unroll
         for (int m = 0; m < NKB; ++m) {
           const int q4 = lane + 64 * m;
@@ -1021,10 +1057,11 @@ __global__ void __launch_bounds__(256) moe_down_sparse_kernel(
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const uint32_t wd = c4 == 0 ? cw[b][r].x : c4 == 1 ? cw[b][r].y : c4 == 2 ? cw[b][r].z : cw[b][r].w;
-            const f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc[b][r], 0);
-            const f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc[b][r], 1);
-            const f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc[b][r], 2);
-            const f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc[b][r], 3);
+            const float sc = kb < NB ? e8m0_to_f32((sb[b] >> (8 * r)) & 0xFFu) : 0.f;
+            const f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc, 0);
+            const f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc, 1);
+            const f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc, 2);
+            const f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc, 3);
 #pragma unroll
             for (int j = 0; j < TC; ++j) {
               float v = acc[r][j];
@@ -1232,8 +1269,8 @@ static hipError_t launch_down_sparse(int T, int H, int I, int E, int max_slots, 
                                      const float* a, const uint16_t* res, float* y, uint16_t* h, uint16_t* h2,
                                      float* part, unsigned* counters, hipStream_t st) {
   const int nkb = (I / 32 + 7) / 8;
-  dim3 grid(H / kDnRows, down_groups(max_slots));
-  const size_t lds = down_grouped_lds(4, I);
+  dim3 grid(H / kDnRows, down_sparse_groups(T, max_slots > 1 ? (max_slots - 1) / T : 0));
+  const size_t lds = down_grouped_lds(2, I);
 #define WSX_DS_CASE(N)                                                                                          \
   case N:                                                                                                       \
     moe_down_sparse_kernel<N><<<grid, 256, lds, st>>>(T, H, I, E, max_slots, w2c, w2s, sh2c, sh2s, el, sw, a,  \
@@ -1253,7 +1290,7 @@ hipError_t launch_down(int T, int H, int I, int E, int k, const uint8_t* w2c, co
                        hipStream_t st) {
   const int max_slots = T * k + 1;
   if (T > WSX_MAX_T) {
-    if (!part || !counters || !down_grouped_ok(4, H, I)) return hipErrorInvalidValue;
+    if (!part || !counters || !down_grouped_ok(2, H, I)) return hipErrorInvalidValue;
     return launch_down_sparse(T, H, I, E, max_slots, w2c, w2s, sh2c, sh2s, el, sw, a, res, y, h, h2, part, counters, st);
   }
   if (part && counters && down_grouped_ok(T, H, I)) {

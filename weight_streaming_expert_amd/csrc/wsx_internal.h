@@ -37,6 +37,7 @@ hipError_t launch_down(int T, int H, int I, int E, int k, const uint8_t* w2c, co
 // The grouped down kernel for several tokens: slot groups per row tile, the
 // bytes of its partial sums ([groups][T][H] fp32) and its per-tile counters.
 int down_groups(int max_slots);
+int down_sparse_groups(int T, int k);   // the same for 5..16 tokens (sparse token lists)
 bool down_grouped_ok(int T, int H, int I);
 
 // moe_w4a8.hip: W4A8 experts (MXFP4 weights x MXFP8 activations on the matrix cores)
