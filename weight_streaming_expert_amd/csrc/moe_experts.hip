@@ -13,11 +13,14 @@
 //            E2M1 nibbles in registers with the hardware converter, applies the
 //            E8M0 block scale per 32 elements and writes a = silu(g) * u (fp32).
 //            Surplus workgroups (slots past the active count) exit at once.
-//   down     grid (H/8): workgroup owns 8 output rows and loops over every
-//            active slot (its 4 wavefronts take slots round-robin), then sums
-//            the four wavefront partials in a fixed order, adds the residual
-//            and rounds to bf16.  The order never depends on timing, so the
-//            result is bit-reproducible.
+//   down     one token: grid (H/8), a workgroup owns 8 output rows and loops
+//            over every active slot (its 4 wavefronts take slots round-robin),
+//            then sums the four wavefront partials in a fixed order, adds the
+//            residual and rounds to bf16.  2..16 tokens: (32-row tile, group
+//            of four slots) workgroups over expert-sorted token lists, the
+//            groups' partials added in group order by the tile's last
+//            workgroup.  The order never depends on timing, so the result is
+//            bit-reproducible.
 #include "wsx_device.h"
 #include "wsx_internal.h"
 
@@ -759,187 +762,29 @@ __global__ void __launch_bounds__(256) moe_down1_kernel(int H, int I, int E, int
 
 // ---------------------------------------------------------------- down for several tokens
 
-// Down + weighted combine + residual for T >= 2 tokens.  Workgroup (tile, g)
-// owns rows n0 .. n0+31 of y for the slots 4g .. 4g+3, one slot per wavefront.
-// Each wavefront stages its slot's [T][I] activations in LDS once (32-value
-// blocks at a 36-float stride, so the eight block columns a load touches fall
-// in distinct banks); lane (kg, rq) then takes rows n0 + 4 rq .. +3 over the MX
-// blocks kg, kg + 8, ...  The E2M1 codes are decoded already multiplied by
-// their power-of-two block scale (exact), so every product equals the
-// oracle's.  The four slot partials are summed in slot order, written as the
-// group's partial, and the last workgroup of the tile adds the groups in group
-// order and the residual, so the result never depends on timing.
-constexpr int kDnRows = 32;
-
-__device__ __forceinline__ int dpos(int i) { return (i >> 5) * 36 + (i & 31); }
-
-template <int T, int NKB>
-__global__ void __launch_bounds__(256) moe_down_grouped_kernel(
-    int H, int I, int E, int max_slots, const uint8_t* __restrict__ w2c, const uint8_t* __restrict__ w2s,
-    const uint8_t* __restrict__ sh2c, const uint8_t* __restrict__ sh2s, const int32_t* __restrict__ expert_list,
-    const float* __restrict__ slot_w, const float* __restrict__ a_in, const uint16_t* __restrict__ residual,
-    float* __restrict__ out_y, uint16_t* __restrict__ out_h, uint16_t* __restrict__ out_h2, float* part,
-    unsigned* counters) {
-  const int s = 4 * (int)blockIdx.y + (int)(threadIdx.x >> 6);
-  int n_active = expert_list[0];
-  const int e_slot = s < max_slots - 1 ? expert_list[1 + s] : -1;
-  n_active = n_active < 0 ? 0 : (n_active > max_slots - 1 ? max_slots - 1 : n_active);
-  const bool has_sh = sh2c != nullptr;
-  const int nslots = n_active + (has_sh ? 1 : 0);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int kg = lane & 7, rq = lane >> 3;
-  const int n0 = blockIdx.x * kDnRows;
-  const int g = blockIdx.y;
-  const int NB = I / 32;
-  const int lstride = NB * 36;   // floats per token row in LDS
-  extern __shared__ __attribute__((aligned(16))) float as[];   // [4][T][lstride]
-  __shared__ float yw[4][T][kDnRows];
-  __shared__ int flag;
-  float* aw = as + (size_t)wave * T * lstride;
-
-  float acc[4][T];
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int t = 0; t < T; ++t) acc[r][t] = 0.f;
-  // routed slot s < n_active, or part v = s - n_active of the shared expert
-  // (tokens 4 v .. 4 v + 3), whose activations sit in slot n_active
-  const bool shared_part = has_sh && s >= n_active && s - n_active < (T + 3) / 4;
-  const uint8_t *C = nullptr, *S = nullptr;
-  bool active = false;
-  if (s < n_active) {
-    active = e_slot >= 0 && e_slot < E;
-    if (active) {
-      C = w2c + (size_t)e_slot * ((size_t)H * (I / 2));
-      S = w2s + (size_t)e_slot * ((size_t)H * (I / 32));
-    }
-  } else if (shared_part) {
-    active = true;
-    C = sh2c;
-    S = sh2s;
-  }
-  const int as_slot = s < n_active ? s : n_active;
-  if (active) {
-    // weights first (their latency overlaps the staging)
-    const size_t rowc = I / 2, rows = I / 32;
-    uint4 cw[NKB][4];
-    float sc[NKB][4];
-#pragma unroll
-    for (int b = 0; b < NKB; ++b) {
-      const int kb = kg + 8 * b;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = n0 + 4 * rq + r;
-        cw[b][r] = kb < NB ? ld16(C + row * rowc + (size_t)kb * 16) : make_uint4(0, 0, 0, 0);
-        sc[b][r] = kb < NB ? e8m0_to_f32(S[row * rows + kb]) : 0.f;
-      }
-    }
-    // this slot's activations -> LDS, every load issued before the first
-    // store (T*I/4 chunks over the 64 lanes; I <= 256 * NKB)
-    const float4* src = reinterpret_cast<const float4*>(a_in + (size_t)s * T * I);
-    const int nq = T * I / 4;
-    float4 av4[T * NKB];
-#pragma unroll
-    for (int j = 0; j < T * NKB; ++j) {
-      const int q = lane + 64 * j;
-      av4[j] = q < nq ? src[q] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-#pragma unroll
-    for (int j = 0; j < T * NKB; ++j) {
-      const int q = lane + 64 * j;
-      if (q < nq) {
-        const int t = (4 * q) / I, i = (4 * q) % I;
-        *reinterpret_cast<float4*>(aw + t * lstride + dpos(i)) = av4[j];
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < NKB; ++b) {
-      const int kb = kg + 8 * b;
-      if (kb >= NB) continue;
-#pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        float av[T][8];
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-          const float4* ap = reinterpret_cast<const float4*>(aw + t * lstride + kb * 36 + c4 * 8);
-          const float4 v0 = ap[0], v1 = ap[1];
-          av[t][0] = v0.x; av[t][1] = v0.y; av[t][2] = v0.z; av[t][3] = v0.w;
-          av[t][4] = v1.x; av[t][5] = v1.y; av[t][6] = v1.z; av[t][7] = v1.w;
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint32_t wd = c4 == 0 ? cw[b][r].x : c4 == 1 ? cw[b][r].y : c4 == 2 ? cw[b][r].z : cw[b][r].w;
-          const f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc[b][r], 0);
-          const f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc[b][r], 1);
-          const f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc[b][r], 2);
-          const f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc[b][r], 3);
-#pragma unroll
-          for (int t = 0; t < T; ++t) {
-            float v = acc[r][t];
-            v = fmaf(p0.x, av[t][0], v);
-            v = fmaf(p0.y, av[t][1], v);
-            v = fmaf(p1.x, av[t][2], v);
-            v = fmaf(p1.y, av[t][3], v);
-            v = fmaf(p2.x, av[t][4], v);
-            v = fmaf(p2.y, av[t][5], v);
-            v = fmaf(p3.x, av[t][6], v);
-            v = fmaf(p3.y, av[t][7], v);
-            acc[r][t] = v;
-          }
-        }
-      }
-    }
-    float wt[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) wt[t] = (s < n_active) ? slot_w[s * T + t] : 1.0f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int t = 0; t < T; ++t) acc[r][t] *= wt[t];
-  }
-  // sum over the 8 lanes of a row group (fixed DPP tree), one slot per wavefront
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const float v = sum8(acc[r][t]);
-      if (kg == 0) yw[wave][t][4 * rq + r] = v;
-    }
-  __syncthreads();
-  if (threadIdx.x < kDnRows * T) {
-    const int t = threadIdx.x / kDnRows, rr = threadIdx.x % kDnRows;
-    const float v = ((yw[0][t][rr] + yw[1][t][rr]) + yw[2][t][rr]) + yw[3][t][rr];
-    st_dev(part + ((size_t)g * T + t) * H + n0 + rr, v);
-  }
-  if (!last_block_arrived(counters + blockIdx.x * 16, gridDim.y, &flag)) return;
-  if (threadIdx.x < kDnRows * T) {
-    const int t = threadIdx.x / kDnRows, rr = threadIdx.x % kDnRows;
-    const float y = sum_group_partials(part, (int)gridDim.y, T, H, t, n0 + rr);
-    const size_t o = (size_t)t * H + n0 + rr;
-    if (out_y) out_y[o] = y;
-    if (residual) {
-      const uint16_t h = f32_to_bf16_rne(bf16_bits_to_f32(residual[o]) + y);
-      if (out_h) out_h[o] = h;
-      if (out_h2) out_h2[o] = h;
-    }
-  }
-}
-
-// Down + weighted combine + residual for 5..16 tokens, over expert-sorted
+// Down + weighted combine + residual for 2..16 tokens, over expert-sorted
 // token lists: the slots are the active experts in ascending id order, and
 // slot s's tokens are those with a nonzero weight slot_w[s][t].  The shared
 // expert, which serves every token, is split into ceil(T / 4) work slots of
 // four tokens each (after the routed slots), so no wavefront carries all T
-// tokens.  Workgroup (tile, g) owns rows n0 .. n0+31 and the work slots
-// 4g .. 4g+3, one per wavefront, as in the grouped kernel above; a wavefront
-// takes its slot's tokens two at a time, staging their activations in LDS and
-// forming the 32 rows x 2 tokens of partial sums from the same decoded
+// tokens.  Workgroup (tile, g) owns rows n0 .. n0+31 of y and the work slots
+// 4g .. 4g+3, one per wavefront.  A wavefront takes its slot's tokens two at a
+// time, staging their activations in LDS (32-value blocks at a 36-float
+// stride, so the eight block columns a load touches fall in distinct banks);
+// lane (kg, rq) takes rows n0 + 4 rq .. +3 over the MX blocks kg, kg + 8, ...
+// and forms the 4 rows x 2 tokens of partial sums from the same decoded
 // weights, so the work follows the routed (slot, token) pairs, not slots x T.
-// Two tokens per pass keep the registers and the LDS stage small enough for
-// three workgroups per CU (at most two passes per work slot).  Each slot's
-// weighted contribution per (token, row) lands in LDS, the four wavefronts
-// are added in slot order, and the groups
-// are added in group order by the tile's last workgroup.
+// The E2M1 codes are decoded already multiplied by their power-of-two block
+// scale (exact), so every product equals the oracle's.  Two tokens per pass
+// keep the registers and the LDS stage small enough for three workgroups per
+// CU.  Each slot's weighted contribution per (token, row) lands in LDS, the
+// four wavefronts are added in slot order into the group's partial, and the
+// last workgroup of the tile adds the groups in group order and the residual,
+// so the result never depends on timing.
+constexpr int kDnRows = 32;
+
+__device__ __forceinline__ int dpos(int i) { return (i >> 5) * 36 + (i & 31); }
+
 int down_sparse_groups(int T, int k) { return (T * k + (T + 3) / 4 + 3) / 4; }
 
 template <int NKB>
@@ -1243,27 +1088,6 @@ bool down_grouped_ok(int T, int H, int I) {
   return T >= 2 && H % kDnRows == 0 && I / 32 <= 32 && down_grouped_lds(T, I) <= 64 * 1024;
 }
 
-template <int T>
-static hipError_t launch_down_grouped_t(int H, int I, int E, int max_slots, const uint8_t* w2c, const uint8_t* w2s,
-                                        const uint8_t* sh2c, const uint8_t* sh2s, const int32_t* el, const float* sw,
-                                        const float* a, const uint16_t* res, float* y, uint16_t* h, uint16_t* h2,
-                                        float* part, unsigned* counters, hipStream_t st) {
-  const int nkb = (I / 32 + 7) / 8;
-  dim3 grid(H / kDnRows, down_groups(max_slots));
-  const size_t lds = down_grouped_lds(T, I);
-#define WSX_DG_CASE(N)                                                                                        \
-  case N:                                                                                                     \
-    moe_down_grouped_kernel<T, N><<<grid, 256, lds, st>>>(H, I, E, max_slots, w2c, w2s, sh2c, sh2s, el, sw, a, \
-                                                          res, y, h, h2, part, counters);                      \
-    break;
-  switch (nkb) {
-    WSX_DG_CASE(1) WSX_DG_CASE(2) WSX_DG_CASE(3) WSX_DG_CASE(4)
-    default: return hipErrorInvalidValue;
-  }
-#undef WSX_DG_CASE
-  return hipGetLastError();
-}
-
 static hipError_t launch_down_sparse(int T, int H, int I, int E, int max_slots, const uint8_t* w2c, const uint8_t* w2s,
                                      const uint8_t* sh2c, const uint8_t* sh2s, const int32_t* el, const float* sw,
                                      const float* a, const uint16_t* res, float* y, uint16_t* h, uint16_t* h2,
@@ -1289,17 +1113,10 @@ hipError_t launch_down(int T, int H, int I, int E, int k, const uint8_t* w2c, co
                        const uint16_t* res, float* y, uint16_t* h, uint16_t* h2, float* part, unsigned* counters,
                        hipStream_t st) {
   const int max_slots = T * k + 1;
-  if (T > WSX_MAX_T) {
-    if (!part || !counters || !down_grouped_ok(2, H, I)) return hipErrorInvalidValue;
+  // 2..16 tokens: expert-sorted token lists
+  if (T >= 2 && part && counters && down_grouped_ok(2, H, I))
     return launch_down_sparse(T, H, I, E, max_slots, w2c, w2s, sh2c, sh2s, el, sw, a, res, y, h, h2, part, counters, st);
-  }
-  if (part && counters && down_grouped_ok(T, H, I)) {
-    switch (T) {
-      case 2: return launch_down_grouped_t<2>(H, I, E, max_slots, w2c, w2s, sh2c, sh2s, el, sw, a, res, y, h, h2, part, counters, st);
-      case 3: return launch_down_grouped_t<3>(H, I, E, max_slots, w2c, w2s, sh2c, sh2s, el, sw, a, res, y, h, h2, part, counters, st);
-      case 4: return launch_down_grouped_t<4>(H, I, E, max_slots, w2c, w2s, sh2c, sh2s, el, sw, a, res, y, h, h2, part, counters, st);
-    }
-  }
+  if (T > WSX_MAX_T) return hipErrorInvalidValue;
   const bool alds = (size_t)max_slots * T * I * 4 <= kDownLdsLimit;
   if (T == 1 && alds && max_slots <= 12 && (size_t)max_slots * I / 4 <= (size_t)256 * 7) {
     const int njd = (I / 32 + 7) / 8;
