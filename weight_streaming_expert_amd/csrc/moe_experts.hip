@@ -557,7 +557,9 @@ __global__ void __launch_bounds__(256) moe_gateup_mfma_mt_kernel(const uint16_t*
         rb[wave][1][4 * q + r][col] = du[r];
       }
     }
-    __syncthreads();
+    // LDS-only barrier: __syncthreads() would also wait for the next tile's
+    // weight loads, which are meant to stay in flight across it
+    lds_barrier();
     if ((int)threadIdx.x < 16 * T) {
       const int rr = threadIdx.x % 16, t = threadIdx.x / 16;
       const float g = ((rb[0][0][rr][t] + rb[1][0][rr][t]) + rb[2][0][rr][t]) + rb[3][0][rr][t];
