@@ -500,22 +500,40 @@ __global__ void __launch_bounds__(256) moe_gateup_mfma_mt_kernel(const uint16_t*
   const int b0 = wave * 4 * NQ;
   const size_t rowc = H / 2, rows = H / 32;
   const int col = row;   // B operand: lane (col, q), token col
-  auto load_tile = [&](int i0, uint4 (&cw)[2][NQ], float (&sc)[2][NQ]) {
+  // the scale bytes of all of the workgroup's rows, staged in LDS once with
+  // 16-byte loads ([gate | up][row][block]; the tiles' rows are contiguous)
+  constexpr int kMaxNB = 4 * 4 * NQ;   // blocks per row: H / 32 <= 16 NQ
+  __shared__ __attribute__((aligned(16))) uint8_t ss[2][16 * NTI][kMaxNB];
+  {
+    const int nrow = (I - ibase < 16 * NTI ? I - ibase : 16 * NTI);
+    const int n16 = nrow * NB / 16;   // NB % 16 == 0 is not assumed: bytes past n16 * 16 go one at a time
+    for (int h = 0; h < 2; ++h) {
+      const uint8_t* src = S + ((size_t)h * I + ibase) * rows;
+      for (int c = threadIdx.x; c < n16; c += 256) {
+        const uint4 v = ld16(src + (size_t)c * 16);
+        const uint8_t* vb = reinterpret_cast<const uint8_t*>(&v);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int o = c * 16 + e;
+          ss[h][o / NB][o % NB] = vb[e];
+        }
+      }
+      for (int o = n16 * 16 + threadIdx.x; o < nrow * NB; o += 256) ss[h][o / NB][o % NB] = src[o];
+    }
+  }
+  auto load_tile = [&](int i0, uint4 (&cw)[2][NQ]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int r = h * I + i0 + row;
 #pragma unroll
       for (int j = 0; j < NQ; ++j) {
         const int b = b0 + 4 * j + q;
-        const bool ok = b < NB;
-        cw[h][j] = ok ? ld16(C + r * rowc + (size_t)b * 16) : make_uint4(0, 0, 0, 0);
-        sc[h][j] = ok ? e8m0_to_f32(S[r * rows + b]) : 0.f;
+        cw[h][j] = b < NB ? ld16(C + r * rowc + (size_t)b * 16) : make_uint4(0, 0, 0, 0);
       }
     }
   };
   uint4 cw[2][NQ];
-  float sc[2][NQ];
-  load_tile(ibase, cw, sc);
+  load_tile(ibase, cw);
   const bool col_used = col < T && wcol != 0.f;
   uint4 xa[NQ][4];
 #pragma unroll
@@ -534,19 +552,23 @@ __global__ void __launch_bounds__(256) moe_gateup_mfma_mt_kernel(const uint16_t*
     const int i0 = ibase + 16 * ti;
     if (i0 >= I) break;   // the same in every thread
     uint4 nw[2][NQ];
-    float ns[2][NQ];
-    if (ti + 1 < NTI && i0 + 16 < I) load_tile(i0 + 16, nw, ns);
+    if (ti + 1 < NTI && i0 + 16 < I) load_tile(i0 + 16, nw);
     issue_here();
+    if (ti == 0) lds_barrier();   // the staged scales
     f32x4_t dg = {0.f, 0.f, 0.f, 0.f}, du = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
+      const int b = b0 + 4 * j + q;
+      float sc[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) sc[h] = b < NB ? e8m0_to_f32(ss[h][16 * ti + row][b]) : 0.f;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const bf16x8_t bx = __builtin_bit_cast(bf16x8_t, xa[j][m]);
         const uint32_t wg = m == 0 ? cw[0][j].x : m == 1 ? cw[0][j].y : m == 2 ? cw[0][j].z : cw[0][j].w;
         const uint32_t wu = m == 0 ? cw[1][j].x : m == 1 ? cw[1][j].y : m == 2 ? cw[1][j].z : cw[1][j].w;
-        dg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4x8_to_bf16x8(wg, sc[0][j]), bx, dg, 0, 0, 0);
-        du = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4x8_to_bf16x8(wu, sc[1][j]), bx, du, 0, 0, 0);
+        dg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4x8_to_bf16x8(wg, sc[0]), bx, dg, 0, 0, 0);
+        du = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4x8_to_bf16x8(wu, sc[1]), bx, du, 0, 0, 0);
       }
     }
     float (*rb)[2][16][20] = red[ti & 1];
@@ -570,10 +592,7 @@ __global__ void __launch_bounds__(256) moe_gateup_mfma_mt_kernel(const uint16_t*
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int j = 0; j < NQ; ++j) {
-          cw[h][j] = nw[h][j];
-          sc[h][j] = ns[h][j];
-        }
+        for (int j = 0; j < NQ; ++j) cw[h][j] = nw[h][j];
     }
   }
 }
