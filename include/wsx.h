@@ -18,7 +18,8 @@
  *    row-major along the contraction dimension K: `codes` [N][K/2] with
  *    element 2j in the low nibble of byte j and element 2j+1 in the high
  *    nibble, and `scales` [N][K/32] of E8M0 bytes, byte b scaling elements
- *    32b..32b+31 of its row.
+ *    32b..32b+31 of its row.  Both arrays start 16-byte aligned (the kernels
+ *    read the scale bytes 16 at a time).
  *  - Every argument check runs on the host before anything is enqueued.  On
  *    an error nothing is enqueued and outputs are untouched.  A failed launch
  *    returns WSX_ERR_HIP.  The library never aborts or prints.

@@ -83,6 +83,8 @@ def test_expert_argument_errors():
     assert experts(T=17) == 4
     assert experts(I=32 * 1000) == 4
     assert experts(c2=MIS) == 3
+    assert experts(s13=MIS) == 3 and experts(s2=MIS) == 3
+    assert experts(sh=(FAKE, MIS, FAKE, FAKE)) == 3
     assert experts(wsb=100) == 5
     lib = _lib.load()
     need = lib.wsx_moe_workspace_bytes(1, 2560, 768, 512, 8)

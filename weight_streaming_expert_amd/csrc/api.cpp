@@ -105,7 +105,8 @@ wsx_status check_experts(const uint16_t* x, const uint8_t* w13c, const uint8_t* 
   if (st != WSX_OK) return st;
   if (H < 32 || I < 32 || H % 32 || I % 32) return WSX_ERR_SHAPE;
   if (!experts_shape_supported(H, I)) return WSX_ERR_UNSUPPORTED;
-  if (!a16(x) || !a16(w13c) || !a16(w2c) || (sh13c && (!a16(sh13c) || !a16(sh2c)))) return WSX_ERR_ALIGN;
+  if (!a16(x) || !a16(w13c) || !a16(w2c) || !a16(w13s) || !a16(w2s)) return WSX_ERR_ALIGN;
+  if (sh13c && (!a16(sh13c) || !a16(sh2c) || !a16(sh13s) || !a16(sh2s))) return WSX_ERR_ALIGN;
   return WSX_OK;
 }
 

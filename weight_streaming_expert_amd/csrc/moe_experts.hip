@@ -829,6 +829,7 @@ __global__ void __launch_bounds__(256) moe_down_sparse_kernel(
   const int lstride = NB * 36;   // floats per token row in LDS
   extern __shared__ __attribute__((aligned(16))) float as[];   // [4][TC][lstride]
   __shared__ float yw[4][WSX_MAX_T_MOE][kDnRows];
+  __shared__ __attribute__((aligned(16))) uint8_t lsc[4][kDnRows * 32];   // per wavefront: [row][block], I <= 1024
   __shared__ int flag;
   float* aw = as + (size_t)wave * TC * lstride;
   for (int i = lane; i < WSX_MAX_T_MOE * kDnRows; i += 64) yw[wave][i / kDnRows][i % kDnRows] = 0.f;
@@ -851,19 +852,25 @@ __global__ void __launch_bounds__(256) moe_down_sparse_kernel(
   const int as_slot = s < n_active ? s : n_active;
   if (active) {
     const size_t rowc = I / 2, rows = I / 32;
+    // the tile's E8M0 scale bytes (32 contiguous rows of NB bytes) into this
+    // wavefront's LDS with 16-byte loads, issued before the codes
+    uint8_t* ls = lsc[wave];
+    const int ns16 = kDnRows * NB / 16;
+    const uint4 sv = lane < ns16 ? ld16(S + (size_t)n0 * rows + (size_t)lane * 16) : make_uint4(0, 0, 0, 0);
     uint4 cw[NKB][4];
-    uint32_t sb[NKB];   // the four rows' E8M0 scale bytes, row r in byte r
 #pragma unroll
     for (int b = 0; b < NKB; ++b) {
       const int kb = kg + 8 * b;
-      sb[b] = 0u;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = n0 + 4 * rq + r;
         cw[b][r] = kb < NB ? ld16(C + row * rowc + (size_t)kb * 16) : make_uint4(0, 0, 0, 0);
-        sb[b] |= (kb < NB ? (uint32_t)S[row * rows + kb] : 0u) << (8 * r);
       }
     }
+    if (lane < ns16) *reinterpret_cast<uint4*>(ls + lane * 16) = sv;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // the slot's token list: lane t < T holds token t's weight
     const int v4 = 4 * (s - n_active);
     const float wl = lane < T ? (s < n_active ? slot_w[s * T + lane] : 1.0f) : 0.f;
@@ -923,7 +930,7 @@ __global__ void __launch_bounds__(256) moe_down_sparse_kernel(
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const uint32_t wd = c4 == 0 ? cw[b][r].x : c4 == 1 ? cw[b][r].y : c4 == 2 ? cw[b][r].z : cw[b][r].w;
-            const float sc = kb < NB ? e8m0_to_f32((sb[b] >> (8 * r)) & 0xFFu) : 0.f;
+            const float sc = kb < NB ? e8m0_to_f32(ls[(4 * rq + r) * NB + kb]) : 0.f;
             const f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc, 0);
             const f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc, 1);
             const f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc, 2);
