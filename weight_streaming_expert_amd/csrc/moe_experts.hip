@@ -237,8 +237,13 @@ __global__ void __launch_bounds__(256) moe_gateup1_kernel(const uint16_t* __rest
   const int r = lane >> 4, c = lane & 15;
   const int NB = H / 32;
   const size_t rowc = H / 2, rows = H / 32;
+  // the tile's scale bytes (16 gate rows, then 16 up rows, each set
+  // contiguous) with 16-byte loads into LDS [gate | up][row][block]
+  __shared__ __attribute__((aligned(16))) uint8_t lsc[2][16 * 16 * NJ];
+  const int t16 = (int)threadIdx.x;
+  const uint4 sv = t16 < 2 * NB ? ld16(S + ((size_t)(t16 / NB) * I + i0) * rows + (size_t)(t16 % NB) * 16)
+                                : make_uint4(0, 0, 0, 0);
   uint4 cw[2][NJ];
-  uint32_t sb[2][NJ];
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
     const int ri = i0 + 4 * wave + 2 * st + (r & 1);
@@ -247,7 +252,6 @@ __global__ void __launch_bounds__(256) moe_gateup1_kernel(const uint16_t* __rest
     for (int j = 0; j < NJ; ++j) {
       const int b = c + 16 * j;
       cw[st][j] = (b < NB) ? ld16(C + row * rowc + (size_t)b * 16) : make_uint4(0, 0, 0, 0);
-      sb[st][j] = (b < NB) ? (uint32_t)S[row * rows + b] : 127u;
     }
   }
   issue_here();
@@ -257,6 +261,7 @@ __global__ void __launch_bounds__(256) moe_gateup1_kernel(const uint16_t* __rest
     const int i = threadIdx.x + 256 * q;
     if (i < H / 8) reinterpret_cast<uint4*>(xs)[i] = xv[q];
   }
+  if (t16 < 2 * NB) *reinterpret_cast<uint4*>(&lsc[t16 / NB][(t16 % NB) * 16]) = sv;
   lds_barrier();
   const uint32_t* xs32 = reinterpret_cast<const uint32_t*>(xs);
   uint32_t xr[NJ][16];
@@ -269,11 +274,12 @@ __global__ void __launch_bounds__(256) moe_gateup1_kernel(const uint16_t* __rest
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
     float acc = 0.f;
+    const uint8_t* lrow = &lsc[r >> 1][(4 * wave + 2 * st + (r & 1)) * NB];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int b = c + 16 * j;
       if (b >= NB) continue;
-      acc = fmaf(mx_block_dot(cw[st][j], xr[j]), e8m0_to_f32(sb[st][j]), acc);
+      acc = fmaf(mx_block_dot(cw[st][j], xr[j]), e8m0_to_f32(lrow[b]), acc);
     }
     const int ri = i0 + 4 * wave + 2 * st + (r & 1);
     const float sum = sum16(acc);
