@@ -327,23 +327,35 @@ __global__ void __launch_bounds__(256) moe_gateup_mfma_kernel(const uint16_t* __
   const int b0 = wave * 4 * NQ;   // first MX block of this wavefront's quarter
   const size_t rowc = H / 2, rows = H / 32;
   // weights of both tiles first: lane (row, q) owns block b0 + 4 j + q of its row
+  // the tile's scale bytes (16 gate rows, then 16 up rows, each set
+  // contiguous) with 16-byte loads, staged in LDS with the activations
+  __shared__ __attribute__((aligned(16))) uint8_t lsc[2][16 * 16 * NQ];
+  const int t16 = (int)threadIdx.x;
+  const uint4 sv = t16 < 2 * NB ? ld16(S + ((size_t)(t16 / NB) * I + i0) * rows + (size_t)(t16 % NB) * 16)
+                                : make_uint4(0, 0, 0, 0);
   uint4 cw[2][NQ];
-  float sc[2][NQ];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int r = h * I + i0 + row;
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
       const int b = b0 + 4 * j + q;
-      const bool ok = b < NB;
-      cw[h][j] = ok ? ld16(C + r * rowc + (size_t)b * 16) : make_uint4(0, 0, 0, 0);
-      sc[h][j] = ok ? e8m0_to_f32(S[r * rows + b]) : 0.f;
+      cw[h][j] = b < NB ? ld16(C + r * rowc + (size_t)b * 16) : make_uint4(0, 0, 0, 0);
     }
   }
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
   __shared__ float red[4][2][16][T];
   stage_to_lds<256, (T * 320 + 255) / 256>(x, xs, T * H / 8);
+  if (t16 < 2 * NB) *reinterpret_cast<uint4*>(&lsc[t16 / NB][(t16 % NB) * 16]) = sv;
   __syncthreads();
+  float sc[2][NQ];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const int b = b0 + 4 * j + q;
+      sc[h][j] = b < NB ? e8m0_to_f32(lsc[h][row * NB + b]) : 0.f;
+    }
   f32x4_t dg = {0.f, 0.f, 0.f, 0.f}, du = {0.f, 0.f, 0.f, 0.f};
   const int col = row;   // B operand: lane (col, q)
 #pragma unroll
