@@ -167,14 +167,26 @@ __global__ void __launch_bounds__(256) moe_gateup_w4a8_kernel(
   const int NB = H / 32;
   // weights first: wavefront w takes rows (w >> 1) * I + i0 + 16 (w & 1) + r16
   const int row = (wave >> 1) * I + i0 + 16 * (wave & 1) + r16;
+  // the weights' scale bytes (32 gate rows, then 32 up rows, each set
+  // contiguous) with 16-byte loads, staged in LDS beside the activations
+  __shared__ __attribute__((aligned(16))) uint8_t lsc[2][32 * 4 * NS];
+  uint4 sv[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int t16 = (int)threadIdx.x + 256 * u;
+    sv[u] = t16 < 4 * NB ? ld16(S + ((size_t)(t16 / (2 * NB)) * I + i0) * NB + (size_t)(t16 % (2 * NB)) * 16)
+                         : make_uint4(0, 0, 0, 0);
+  }
   uint4 cw[NS];
-  int sw[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int b = 4 * s + g;
-    const bool ok = b < NB;
-    cw[s] = ok ? ld16(C + (size_t)row * (H / 2) + (size_t)b * 16) : make_uint4(0, 0, 0, 0);
-    sw[s] = ok ? (int)S[(size_t)row * NB + b] : 127;
+    cw[s] = b < NB ? ld16(C + (size_t)row * (H / 2) + (size_t)b * 16) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int t16 = (int)threadIdx.x + 256 * u;
+    if (t16 < 4 * NB) *reinterpret_cast<uint4*>(&lsc[t16 / (2 * NB)][(t16 % (2 * NB)) * 16]) = sv[u];
   }
   // the T input rows, quantized into LDS: codes [T][H], scales [T][NB]
   extern __shared__ __attribute__((aligned(16))) uint8_t sm[];
@@ -193,6 +205,13 @@ __global__ void __launch_bounds__(256) moe_gateup_w4a8_kernel(
     xs[t * NB + kb] = (uint8_t)sb;
   }
   __syncthreads();
+  int sw[NS];
+  const uint8_t* lrow = &lsc[wave >> 1][(16 * (wave & 1) + r16) * NB];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int b = 4 * s + g;
+    sw[s] = b < NB ? (int)lrow[b] : 127;
+  }
   v4f_t acc = {0.f, 0.f, 0.f, 0.f};
   const bool col = r16 < T;
 #pragma unroll
@@ -247,20 +266,34 @@ __global__ void __launch_bounds__(256) moe_down_w4a8_kernel(
   const int n0 = blockIdx.x * 16;
   const int NB = I / 32;
   const bool col = r16 < T;
+  __shared__ __attribute__((aligned(16))) uint8_t lsd[4][16 * 4 * NSD];   // per wavefront: [row][block]
   v4f_t tot = {0.f, 0.f, 0.f, 0.f};
   for (int s = wave; s < nslots; s += 4) {
     const uint8_t *C, *S;
     if (!w4a8_slot(s, n_active, has_sh, E, el, w2c, w2s, sh2c, sh2s, (size_t)H * (I / 2), (size_t)H * NB, &C, &S))
       continue;
     const int row = n0 + r16;
+    // the 16 rows' scale bytes (contiguous) into this wavefront's LDS with
+    // 16-byte loads, issued before the codes
+    const uint4 sv = lane < NB ? ld16(S + (size_t)n0 * NB + (size_t)lane * 16) : make_uint4(0, 0, 0, 0);
     uint4 cw[NSD];
+#pragma unroll
+    for (int st = 0; st < NSD; ++st) {
+      const int b = 4 * st + g;
+      cw[st] = b < NB ? ld16(C + (size_t)row * (I / 2) + (size_t)b * 16) : make_uint4(0, 0, 0, 0);
+    }
+    // the previous slot's reads of this buffer are done (one wavefront, in order)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (lane < NB) *reinterpret_cast<uint4*>(&lsd[wave][lane * 16]) = sv;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     int sw[NSD];
 #pragma unroll
     for (int st = 0; st < NSD; ++st) {
       const int b = 4 * st + g;
-      const bool ok = b < NB;
-      cw[st] = ok ? ld16(C + (size_t)row * (I / 2) + (size_t)b * 16) : make_uint4(0, 0, 0, 0);
-      sw[st] = ok ? (int)S[(size_t)row * NB + b] : 127;
+      sw[st] = b < NB ? (int)lsd[wave][r16 * NB + b] : 127;
     }
     v4f_t c = {0.f, 0.f, 0.f, 0.f};
     const size_t arow = ((size_t)s * T + (col ? r16 : 0)) * I;
