@@ -390,98 +390,15 @@ __global__ void __launch_bounds__(256) moe_gateup_mfma_kernel(const uint16_t* __
   }
 }
 
-// Gate/up + SwiGLU for 5..16 tokens (a small batch or a longer draft), on the
-// matrix cores as above with the tokens as the MFMA's columns; the token
-// columns take their activations straight from global memory (the T rows are
-// read by every workgroup and stay in the caches), so no LDS stage limits T.
-template <int NQ>
-__global__ void __launch_bounds__(256) moe_gateup_mfma_g_kernel(const uint16_t* __restrict__ x, int T, int H, int I,
-                                                                int E, int max_slots, const uint8_t* __restrict__ w13c,
-                                                                const uint8_t* __restrict__ w13s,
-                                                                const uint8_t* __restrict__ sh13c,
-                                                                const uint8_t* __restrict__ sh13s,
-                                                                const int32_t* __restrict__ expert_list,
-                                                                float* __restrict__ a_out) {
-  const int slot = blockIdx.y;
-  int n_active = expert_list[0];
-  n_active = n_active < 0 ? 0 : (n_active > max_slots - 1 ? max_slots - 1 : n_active);
-  const bool has_sh = sh13c != nullptr;
-  const int i0 = blockIdx.x * 16;
-  const uint8_t *C, *S;
-  if (!slot_expert(slot, n_active, has_sh, E, expert_list, w13c, w13s, sh13c, sh13s, (size_t)2 * I * (H / 2),
-                   (size_t)2 * I * (H / 32), &C, &S)) {
-    if (slot < n_active + (has_sh ? 1 : 0))
-      for (int i = threadIdx.x; i < 16 * T; i += 256) a_out[((size_t)slot * T + i / 16) * I + i0 + (i % 16)] = 0.f;
-    return;
-  }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row = lane & 15, q = lane >> 4;
-  const int NB = H / 32;
-  const int b0 = wave * 4 * NQ;
-  const size_t rowc = H / 2, rows = H / 32;
-  uint4 cw[2][NQ];
-  float sc[2][NQ];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int r = h * I + i0 + row;
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      const int b = b0 + 4 * j + q;
-      const bool ok = b < NB;
-      cw[h][j] = ok ? ld16(C + r * rowc + (size_t)b * 16) : make_uint4(0, 0, 0, 0);
-      sc[h][j] = ok ? e8m0_to_f32(S[r * rows + b]) : 0.f;
-    }
-  }
-  // rows of 20 floats: the four rows 4q + r that one store touches then
-  // fall 16 banks apart (a 16-float row put them all in the same banks)
-  __shared__ float red[4][2][16][20];
-  static_assert(WSX_MAX_T_MOE <= 20, "reduction tile columns");
-  f32x4_t dg = {0.f, 0.f, 0.f, 0.f}, du = {0.f, 0.f, 0.f, 0.f};
-  const int col = row;   // B operand: lane (col, q), token col
-  // every activation chunk of this wavefront's quarter, issued together with
-  // the weights above (one round trip, not one per step)
-  uint4 xa[NQ][4];
-#pragma unroll
-  for (int j = 0; j < NQ; ++j) {
-    const int b = b0 + 4 * j + q;
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      xa[j][m] = (col < T && b < NB) ? ld16(x + (size_t)col * H + b * 32 + m * 8) : make_uint4(0, 0, 0, 0);
-  }
-#pragma unroll
-  for (int j = 0; j < NQ; ++j) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const bf16x8_t bx = __builtin_bit_cast(bf16x8_t, xa[j][m]);
-      const uint32_t wg = m == 0 ? cw[0][j].x : m == 1 ? cw[0][j].y : m == 2 ? cw[0][j].z : cw[0][j].w;
-      const uint32_t wu = m == 0 ? cw[1][j].x : m == 1 ? cw[1][j].y : m == 2 ? cw[1][j].z : cw[1][j].w;
-      dg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4x8_to_bf16x8(wg, sc[0][j]), bx, dg, 0, 0, 0);
-      du = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4x8_to_bf16x8(wu, sc[1][j]), bx, du, 0, 0, 0);
-    }
-  }
-  if (col < T) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      red[wave][0][4 * q + r][col] = dg[r];
-      red[wave][1][4 * q + r][col] = du[r];
-    }
-  }
-  __syncthreads();
-  if ((int)threadIdx.x < 16 * T) {
-    const int rr = threadIdx.x % 16, t = threadIdx.x / 16;
-    const float g = ((red[0][0][rr][t] + red[1][0][rr][t]) + red[2][0][rr][t]) + red[3][0][rr][t];
-    const float u = ((red[0][1][rr][t] + red[1][1][rr][t]) + red[2][1][rr][t]) + red[3][1][rr][t];
-    a_out[((size_t)slot * T + t) * I + i0 + rr] = silu(g) * u;
-  }
-}
-
-// The same contraction for 5..16 tokens with four 16-row tiles per
-// workgroup: each wavefront keeps its quarter of K of all T token columns in
-// registers (loaded once, with the first tile's weights) and reuses it for
-// the workgroup's tiles, whose gate/up rows stream one tile ahead; so the
-// activations are read once per 64 rows instead of once per 16.  Each tile's
-// four quarter sums meet in LDS (double-buffered, one barrier per tile) and are
-// added in wavefront order, as in moe_gateup_mfma_g_kernel.
+// The same contraction for 5..16 tokens (a small batch or a longer draft),
+// with the tokens as the MFMA's columns and four 16-row tiles per workgroup:
+// each wavefront keeps its quarter of K of all T token columns in registers
+// (loaded once from global memory, with the first tile's weights) and reuses
+// it for the workgroup's tiles, whose gate/up rows stream one tile ahead; so
+// the activations are read once per 64 rows instead of once per 16, and no
+// LDS stage limits T.  The workgroup's scale bytes are staged in LDS once.
+// Each tile's four quarter sums meet in LDS (double-buffered, one barrier per
+// tile) and are added in wavefront order.
 template <int NQ, int NTI>
 __global__ void __launch_bounds__(256) moe_gateup_mfma_mt_kernel(const uint16_t* __restrict__ x, int T, int H, int I,
                                                                  int E, int max_slots, const uint8_t* __restrict__ w13c,
