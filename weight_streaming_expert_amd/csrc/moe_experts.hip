@@ -752,11 +752,14 @@ __global__ void __launch_bounds__(256) moe_down_sparse_kernel(
     unsigned* counters) {
   constexpr int TC = 2;   // tokens per pass
   const int s = 4 * (int)blockIdx.y + (int)(threadIdx.x >> 6);   // work slot
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the list entry, the active count and the slot's row of weights in one
+  // round trip (the row is only used if s turns out to be a routed slot)
   int n_active = expert_list[0];
   const int e_slot = s < max_slots - 1 ? expert_list[1 + s] : -1;
+  const float wrow = (s < max_slots - 1 && lane < T) ? slot_w[s * T + lane] : 0.f;
   n_active = n_active < 0 ? 0 : (n_active > max_slots - 1 ? max_slots - 1 : n_active);
   const bool has_sh = sh2c != nullptr;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kg = lane & 7, rq = lane >> 3;
   const int n0 = blockIdx.x * kDnRows;
   const int g = blockIdx.y;
@@ -808,7 +811,7 @@ __global__ void __launch_bounds__(256) moe_down_sparse_kernel(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // the slot's token list: lane t < T holds token t's weight
     const int v4 = 4 * (s - n_active);
-    const float wl = lane < T ? (s < n_active ? slot_w[s * T + lane] : 1.0f) : 0.f;
+    const float wl = lane < T ? (s < n_active ? wrow : 1.0f) : 0.f;
     unsigned long long tm = s < n_active ? __ballot(lane < T && wl != 0.f) : __ballot(lane >= v4 && lane < v4 + 4 && lane < T);
     while (tm) {
       int tok[TC];
