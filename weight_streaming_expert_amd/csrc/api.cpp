@@ -212,7 +212,8 @@ wsx_status moe_expert_gemv_w4a8(const uint16_t* x, const uint8_t* w13_codes, con
   if ((st = check_ws(ws, ws_bytes, L.total)) != WSX_OK) return st;
   return hip_status(launch_w4a8_experts(x, T, H, I, E, k, w13_codes, w13_scales, w2_codes, w2_scales, sh13_codes,
                                         sh13_scales, sh2_codes, sh2_scales, expert_list, slot_w, residual, out_y,
-                                        out_h, act_out, (char*)ws + L.a, S(stream)));
+                                        out_h, act_out, (char*)ws + L.a, reinterpret_cast<float*>((char*)ws + L.part),
+                                        reinterpret_cast<unsigned*>((char*)ws + L.dcnt), S(stream)));
 }
 
 wsx_status lm_head_quantize_fp8(const uint16_t* w, int V, int K, uint8_t* q, float* row_scale, void* stream) {

@@ -22,6 +22,7 @@
 //            workgroup.  The order never depends on timing, so the result is
 //            bit-reproducible.
 #include "wsx_device.h"
+#include "partials_device.h"
 #include "wsx_internal.h"
 
 namespace wsx {
@@ -63,24 +64,6 @@ __device__ __forceinline__ bool slot_expert(int slot, int n_active, bool has_sh,
   }
   if (slot == n_active && has_sh) { *C = shc; *S = shs; return true; }
   return false;
-}
-
-// Sum, in group order, of the ng partials part[(g T + t) H + n] (written by
-// other workgroups with device-coherent stores): the loads go out eight at a
-// time, so the tail costs one coherent round trip per eight groups, not one
-// per group.
-__device__ __forceinline__ float sum_group_partials(const float* part, int ng, int T, int H, int t, int n) {
-  float y = 0.f;
-  for (int g0 = 0; g0 < ng; g0 += 8) {
-    float v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      v[j] = g0 + j < ng ? __uint_as_float(ld_coh4(part, (uint32_t)(((size_t)(g0 + j) * T + t) * H + n) * 4)) : 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (g0 + j < ng) y += v[j];
-  }
-  return y;
 }
 
 // slot_expert with the slot's list entry already loaded (read beside the

@@ -32,6 +32,7 @@
 //            then the four partials are added in wavefront order with the
 //            residual: the order never depends on timing.
 #include "wsx_device.h"
+#include "partials_device.h"
 #include "wsx_internal.h"
 
 namespace wsx {
@@ -251,12 +252,25 @@ __global__ void __launch_bounds__(256) moe_gateup_w4a8_kernel(
 
 // ---------------------------------------------------------------- down + combine + residual
 
+// Workgroup (16-row tile, group g) takes the slots 8 g .. 8 g + 7, two per
+// wavefront (s = 8 g + wave + 4 i), both slots' rows and scale bytes
+// requested at once; the four wavefront sums are added in wavefront order.
+// With one group the workgroup writes the output itself; otherwise each
+// group's sum is a partial and the tile's last workgroup adds the groups in
+// group order and the residual.  Splitting the slots over workgroups keeps
+// every wavefront to two weight fetches issued together instead of one
+// dependent fetch per slot.
+constexpr int kW4A8DownSpw = 2;   // slots per wavefront
+int w4a8_down_groups(int max_slots) { return (max_slots + 4 * kW4A8DownSpw - 1) / (4 * kW4A8DownSpw); }
+
 template <int NSD>   // matrix-core steps of 128 covering I
 __global__ void __launch_bounds__(256) moe_down_w4a8_kernel(
     int T, int H, int I, int E, int max_slots, const uint8_t* __restrict__ w2c, const uint8_t* __restrict__ w2s,
     const uint8_t* __restrict__ sh2c, const uint8_t* __restrict__ sh2s, const int32_t* __restrict__ el,
     const float* __restrict__ slot_w, const uint8_t* __restrict__ aq, const uint8_t* __restrict__ aqs,
-    const uint16_t* __restrict__ residual, float* __restrict__ out_y, uint16_t* __restrict__ out_h) {
+    const uint16_t* __restrict__ residual, float* __restrict__ out_y, uint16_t* __restrict__ out_h, float* part,
+    unsigned* counters) {
+  constexpr int SPW = kW4A8DownSpw;
   int n_active = el[0];
   n_active = n_active < 0 ? 0 : (n_active > max_slots - 1 ? max_slots - 1 : n_active);
   const bool has_sh = sh2c != nullptr;
@@ -266,34 +280,42 @@ __global__ void __launch_bounds__(256) moe_down_w4a8_kernel(
   const int n0 = blockIdx.x * 16;
   const int NB = I / 32;
   const bool col = r16 < T;
-  __shared__ __attribute__((aligned(16))) uint8_t lsd[4][16 * 4 * NSD];   // per wavefront: [row][block]
-  v4f_t tot = {0.f, 0.f, 0.f, 0.f};
-  for (int s = wave; s < nslots; s += 4) {
-    const uint8_t *C, *S;
-    if (!w4a8_slot(s, n_active, has_sh, E, el, w2c, w2s, sh2c, sh2s, (size_t)H * (I / 2), (size_t)H * NB, &C, &S))
-      continue;
-    const int row = n0 + r16;
-    // the 16 rows' scale bytes (contiguous) into this wavefront's LDS with
-    // 16-byte loads, issued before the codes
-    const uint4 sv = lane < NB ? ld16(S + (size_t)n0 * NB + (size_t)lane * 16) : make_uint4(0, 0, 0, 0);
-    uint4 cw[NSD];
+  const int row = n0 + r16;
+  __shared__ __attribute__((aligned(16))) uint8_t lsd[4][SPW][16 * 4 * NSD];   // per wavefront and slot: [row][block]
+  __shared__ int flag;
+  // both slots' rows and scale bytes first (16 contiguous rows of scales per slot)
+  bool use[SPW];
+  uint4 sv[SPW];
+  uint4 cw[SPW][NSD];
+#pragma unroll
+  for (int i = 0; i < SPW; ++i) {
+    const int s = (int)blockIdx.y * 4 * SPW + wave + 4 * i;
+    const uint8_t *C = nullptr, *S = nullptr;
+    use[i] = s < nslots &&
+             w4a8_slot(s, n_active, has_sh, E, el, w2c, w2s, sh2c, sh2s, (size_t)H * (I / 2), (size_t)H * NB, &C, &S);
+    sv[i] = use[i] && lane < NB ? ld16(S + (size_t)n0 * NB + (size_t)lane * 16) : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int st = 0; st < NSD; ++st) {
       const int b = 4 * st + g;
-      cw[st] = b < NB ? ld16(C + (size_t)row * (I / 2) + (size_t)b * 16) : make_uint4(0, 0, 0, 0);
+      cw[i][st] = use[i] && b < NB ? ld16(C + (size_t)row * (I / 2) + (size_t)b * 16) : make_uint4(0, 0, 0, 0);
     }
-    // the previous slot's reads of this buffer are done (one wavefront, in order)
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    if (lane < NB) *reinterpret_cast<uint4*>(&lsd[wave][lane * 16]) = sv;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+#pragma unroll
+  for (int i = 0; i < SPW; ++i)
+    if (use[i] && lane < NB) *reinterpret_cast<uint4*>(&lsd[wave][i][lane * 16]) = sv[i];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  v4f_t tot = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < SPW; ++i) {
+    if (!use[i]) continue;   // uniform across the wavefront
+    const int s = (int)blockIdx.y * 4 * SPW + wave + 4 * i;
     int sw[NSD];
 #pragma unroll
     for (int st = 0; st < NSD; ++st) {
       const int b = 4 * st + g;
-      sw[st] = b < NB ? (int)lsd[wave][r16 * NB + b] : 127;
+      sw[st] = b < NB ? (int)lsd[wave][i][r16 * NB + b] : 127;
     }
     v4f_t c = {0.f, 0.f, 0.f, 0.f};
     const size_t arow = ((size_t)s * T + (col ? r16 : 0)) * I;
@@ -302,22 +324,39 @@ __global__ void __launch_bounds__(256) moe_down_w4a8_kernel(
       v8i_t b = {0, 0, 0, 0, 0, 0, 0, 0};
       int sb = 127;
       if (col) b_operand(aq + arow, aqs + arow / 32, I, st, g, b, sb);
-      const v8i_t a = {(int)cw[st].x, (int)cw[st].y, (int)cw[st].z, (int)cw[st].w, 0, 0, 0, 0};
+      const v8i_t a = {(int)cw[i][st].x, (int)cw[i][st].y, (int)cw[i][st].z, (int)cw[i][st].w, 0, 0, 0, 0};
       c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, kFmtFp4, kFmtFp8, 0, sw[st], 0, sb);
     }
     const float wt = col ? (s < n_active ? slot_w[s * T + r16] : 1.0f) : 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) tot[q] = fmaf(wt, c[q], tot[q]);
   }
-  __shared__ float part[4][16][17];   // [wavefront][row][token]
+  __shared__ float pw[4][16][17];   // [wavefront][row][token]
   if (col) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) part[wave][4 * g + q][r16] = tot[q];
+    for (int q = 0; q < 4; ++q) pw[wave][4 * g + q][r16] = tot[q];
   }
   __syncthreads();
+  if (gridDim.y == 1) {   // every slot in this workgroup: no partials
+    if ((int)threadIdx.x < 16 * T) {
+      const int rr = threadIdx.x & 15, t = threadIdx.x >> 4;
+      const float y = ((pw[0][rr][t] + pw[1][rr][t]) + pw[2][rr][t]) + pw[3][rr][t];
+      const size_t o = (size_t)t * H + n0 + rr;
+      if (out_y) out_y[o] = y;
+      if (residual && out_h) out_h[o] = f32_to_bf16_rne(bf16_bits_to_f32(residual[o]) + y);
+    }
+    return;
+  }
   if ((int)threadIdx.x < 16 * T) {
     const int rr = threadIdx.x & 15, t = threadIdx.x >> 4;
-    const float y = ((part[0][rr][t] + part[1][rr][t]) + part[2][rr][t]) + part[3][rr][t];
+    const float v = ((pw[0][rr][t] + pw[1][rr][t]) + pw[2][rr][t]) + pw[3][rr][t];
+    st_dev(part + ((size_t)blockIdx.y * T + t) * H + n0 + rr, v);
+  }
+  // the tile's counter: 32-byte stride
+  if (!last_block_arrived(counters + blockIdx.x * 8, gridDim.y, &flag)) return;
+  if ((int)threadIdx.x < 16 * T) {
+    const int rr = threadIdx.x & 15, t = threadIdx.x >> 4;
+    const float y = sum_group_partials(part, (int)gridDim.y, T, H, t, n0 + rr);
     const size_t o = (size_t)t * H + n0 + rr;
     if (out_y) out_y[o] = y;
     if (residual && out_h) out_h[o] = f32_to_bf16_rne(bf16_bits_to_f32(residual[o]) + y);
@@ -357,7 +396,7 @@ hipError_t launch_w4a8_experts(const uint16_t* x, int T, int H, int I, int E, in
                                const uint8_t* w13s, const uint8_t* w2c, const uint8_t* w2s, const uint8_t* sh13c,
                                const uint8_t* sh13s, const uint8_t* sh2c, const uint8_t* sh2s, const int32_t* el,
                                const float* sw, const uint16_t* res, float* y, uint16_t* h, float* act, void* abuf,
-                               hipStream_t st) {
+                               float* part, unsigned* counters, hipStream_t st) {
   const int max_slots = T * k + 1;
   uint8_t* aq = reinterpret_cast<uint8_t*>(abuf);
   uint8_t* aqs = aq + (((size_t)max_slots * T * I + 15) & ~(size_t)15);
@@ -375,10 +414,11 @@ hipError_t launch_w4a8_experts(const uint16_t* x, int T, int H, int I, int E, in
 #undef WSX_WG
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-#define WSX_WD(N)                                                                                                \
-  case N:                                                                                                        \
-    moe_down_w4a8_kernel<N><<<H / 16, 256, 0, st>>>(T, H, I, E, max_slots, w2c, w2s, sh2c, sh2s, el, sw, aq, aqs, \
-                                                    res, y, h);                                                  \
+  const dim3 gd(H / 16, w4a8_down_groups(max_slots));
+#define WSX_WD(N)                                                                                              \
+  case N:                                                                                                      \
+    moe_down_w4a8_kernel<N><<<gd, 256, 0, st>>>(T, H, I, E, max_slots, w2c, w2s, sh2c, sh2s, el, sw, aq, aqs, res, \
+                                                y, h, part, counters);                                         \
     break;
   switch (steps_case((I + 127) / 128)) {
     WSX_WD(1) WSX_WD(2) WSX_WD(3) WSX_WD(4) WSX_WD(5) WSX_WD(6) WSX_WD(8) WSX_WD(10) WSX_WD(12) WSX_WD(16) WSX_WD(20)

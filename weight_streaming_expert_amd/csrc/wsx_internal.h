@@ -48,7 +48,7 @@ hipError_t launch_w4a8_experts(const uint16_t* x, int T, int H, int I, int E, in
                                const uint8_t* w13s, const uint8_t* w2c, const uint8_t* w2s, const uint8_t* sh13c,
                                const uint8_t* sh13s, const uint8_t* sh2c, const uint8_t* sh2s, const int32_t* el,
                                const float* sw, const uint16_t* res, float* y, uint16_t* h, float* act, void* abuf,
-                               hipStream_t st);
+                               float* part, unsigned* counters, hipStream_t st);
 
 // decode_step.hip: the whole 1-token decode step in one launch
 bool fused_step_supported(int T, int router_dtype, bool has_shared, int H, int I, int E, int k);
