@@ -144,3 +144,22 @@ def test_head_is_deterministic(ops, full_head):
     for _ in range(5):
         b = ops.lm_head_gemv_fp8_argmax(full_head["q"], full_head["s"], x)
         assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("T", [2, 3, 4])
+def test_fp8_multi_row_head_equals_one_row_head(ops, full_head, T):
+    """At 2..4 rows each row's products are added in the 1-token head's order,
+    so its logits and argmax equal the 1-token head's on that row, bit for
+    bit; one workspace serves the calls one after another (its counter and
+    maxima return to zero)."""
+    dev = torch.device("cuda:0")
+    ws = ops.workspace(ops.lm_head_workspace_bytes(T, full_head["q"].shape[0], 2560), dev)
+    for rep in range(2):
+        x = inputs.normal_bf16((21, T, rep), (T, 2560), 1.0)
+        xd = P.to_dev_bf16(x)
+        lg, am = ops.lm_head_gemv_fp8_argmax(full_head["q"], full_head["s"], xd, ws=ws)
+        lg, am = P.np_(lg), P.np_(am)
+        for t in range(T):
+            l1, a1 = ops.lm_head_gemv_fp8_argmax(full_head["q"], full_head["s"], xd[t:t + 1].contiguous())
+            assert np.array_equal(lg[t], P.np_(l1)[0]), (T, t)
+            assert int(am[t]) == int(P.np_(a1)[0]), (T, t)

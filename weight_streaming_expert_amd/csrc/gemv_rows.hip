@@ -297,6 +297,127 @@ __device__ __forceinline__ void head_group_load(__amdgpu_buffer_rsrc_t W, const 
   if (WT == W_FP8 && ok && c == 0) g.sc = row_scale[row];
 }
 
+// The wide FP8 head for 2..4 tokens (the verify pass's rows): the row
+// streaming of lm_head_wide_kernel, with the TT activation rows staged in LDS
+// and each granule's 16 codes converted once and used for every token.  Per
+// token the products are added in exactly the 1-token kernel's order, so each
+// token's logits equal the 1-token head's bit for bit.  Per token, every
+// workgroup joins its best (value, row) to a 64-bit atomic max, and the last
+// workgroup publishes the argmaxes.
+template <int TT, int GPL, int RL>
+__global__ void __launch_bounds__(1024) lm_head_wide_t_kernel(const uint8_t* __restrict__ W,
+                                                              const float* __restrict__ row_scale, int V, int K,
+                                                              const uint16_t* __restrict__ x, float* __restrict__ logits,
+                                                              int32_t* __restrict__ argmax, unsigned* counter,
+                                                              unsigned long long* best) {
+  constexpr int RPW = 64 / RL, NW = 16, GS = 48;   // LayHead: 16 bf16 in 48 bytes per granule
+  constexpr int XC = (TT * 2560 / 8 + 1023) / 1024;   // 16-byte input chunks per thread (K <= 2560)
+  extern __shared__ __attribute__((aligned(16))) uint8_t xsb[];   // [TT][G][GS]
+  __shared__ float wv_[NW][TT];
+  __shared__ int wi_[NW][TT];
+  __shared__ int flag;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, c = lane % RL;
+  const int G = K / 16;
+  const uint32_t row_bytes = (uint32_t)K;
+  const __amdgpu_buffer_rsrc_t Wr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(W), 0, 0x7FFFFFFF, 0x00020000);
+  const int NG = (V + RPW - 1) / RPW;
+  const int stride = (int)gridDim.x * NW;
+  const int first = wave * (int)gridDim.x + (int)blockIdx.x;
+  int grp = first < NG ? first : -1;
+  const int nx = K / 8;
+  uint4 xv[XC];
+#pragma unroll
+  for (int q = 0; q < XC; ++q) {
+    const int i = t + 1024 * q;
+    xv[q] = i < TT * nx ? ld16(x + 8 * i) : make_uint4(0, 0, 0, 0);
+  }
+  HeadGroup<W_FP8, GPL, RL> cur;
+  if (grp >= 0) head_group_load<W_FP8, GPL, RL>(Wr, row_scale, V, G, row_bytes, grp, cur);
+  issue_here();
+#pragma unroll
+  for (int q = 0; q < XC; ++q) {
+    const int i = t + 1024 * q;
+    if (i < TT * nx) {
+      const int tok = i / nx, ch = i - tok * nx;
+      *reinterpret_cast<uint4*>(xsb + (size_t)tok * G * GS + (8 * ch / 16) * GS + (8 * ch % 16) * 2) = xv[q];
+    }
+  }
+  lds_barrier();
+  float bv[TT];
+  int bi[TT];
+#pragma unroll
+  for (int k2 = 0; k2 < TT; ++k2) { bv[k2] = -INFINITY; bi[k2] = 0x7FFFFFFF; }
+  while (grp >= 0) {
+    HeadGroup<W_FP8, GPL, RL> nxt;
+    const int ng = grp + stride < NG ? grp + stride : -1;
+    if (ng >= 0) head_group_load<W_FP8, GPL, RL>(Wr, row_scale, V, G, row_bytes, ng, nxt);
+    issue_here();
+    float acc[TT];
+#pragma unroll
+    for (int k2 = 0; k2 < TT; ++k2) acc[k2] = 0.f;
+#pragma unroll
+    for (int j = 0; j < GPL; ++j) {
+      const int g = c + RL * j;
+      if (g < G) {
+        const uint32_t w[4] = {cur.w[j].x, cur.w[j].y, cur.w[j].z, cur.w[j].w};
+        bf16x2_t wp[8];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          wp[2 * d] = fp8x2_to_bf16x2<false>(w[d]);
+          wp[2 * d + 1] = fp8x2_to_bf16x2<true>(w[d]);
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < TT; ++k2) {
+          const uint4* src4 = reinterpret_cast<const uint4*>(xsb + (size_t)k2 * G * GS + g * GS);
+          const uint4 v0 = src4[0], v1 = src4[1];
+          const uint32_t xp[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+          // the order of fp8_granule_dot
+          float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            a0 = dot2(wp[2 * d], as_bf16x2(xp[2 * d + 0]), a0);
+            a1 = dot2(wp[2 * d + 1], as_bf16x2(xp[2 * d + 1]), a1);
+          }
+          acc[k2] += a0 + a1;
+        }
+      }
+    }
+    const int row = grp * RPW + lane / RL;
+#pragma unroll
+    for (int k2 = 0; k2 < TT; ++k2) {
+      float a = sum16(acc[k2]);
+      if constexpr (RL == 32) a += __shfl_xor(a, 16);
+      const float l = a * cur.sc;
+      if (c == 0 && row < V) {
+        if (logits) logits[(size_t)k2 * V + row] = l;
+        if (better(l, row, bv[k2], bi[k2])) { bv[k2] = l; bi[k2] = row; }
+      }
+    }
+    cur = nxt;
+    grp = ng;
+  }
+#pragma unroll
+  for (int k2 = 0; k2 < TT; ++k2) {
+    wave_argmax(bv[k2], bi[k2]);
+    if (lane == 0) { wv_[wave][k2] = bv[k2]; wi_[wave][k2] = bi[k2]; }
+  }
+  lds_barrier();
+  if (t < TT) {
+    float v = wv_[0][t];
+    int i = wi_[0][t];
+    for (int q = 1; q < NW; ++q)
+      if (better(wv_[q][t], wi_[q][t], v, i)) { v = wv_[q][t]; i = wi_[q][t]; }
+    const RankKey key = (v == v) ? rank_key(v, i) : 0ull;   // a NaN never wins
+    __hip_atomic_fetch_max(best + t, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (!last_block_arrived(counter, gridDim.x, &flag)) return;
+  if (t < TT) {
+    const RankKey b = __hip_atomic_load(best + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(best + t, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    argmax[t] = b == 0ull ? -1 : key_id(b);
+  }
+}
+
 // The sampling epilogue of the 1-token head ([ncij] "What happens on a real
 // workload?": temperature, top-p and top-k sampling), fused into its tail.
 // The selection rests on one fact: with the rows split into chunks, the k-th
@@ -1425,6 +1546,27 @@ hipError_t launch_lm_head(int wt, const void* W, const float* s, int V, int K, c
     const hipError_t e = launch_head_wide(wt, W, s, V, K, x, logits, argmax, counter,
                                           reinterpret_cast<unsigned long long*>((char*)ws + 64), st, &done);
     if (done || e != hipSuccess) return e;
+  }
+  if (T >= 2 && !norm && wt == W_FP8 && (K == 2560 || K == 256) && (size_t)V * K < ((size_t)1 << 31)) {
+    // the wide head for the verify pass's rows: one 1024-thread workgroup per CU
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus >= 1) {
+      unsigned long long* best = reinterpret_cast<unsigned long long*>((char*)ws + 64);   // T words
+      const size_t lds = (size_t)T * (K / 16) * 48;
+#define WSX_WT(TV)                                                                                                  \
+  if (T == TV) {                                                                                                    \
+    if (K == 2560)                                                                                                  \
+      lm_head_wide_t_kernel<TV, 10, 16><<<cus, 1024, lds, st>>>((const uint8_t*)W, s, V, K, x, logits, argmax,       \
+                                                                counter, best);                                     \
+    else                                                                                                            \
+      lm_head_wide_t_kernel<TV, 1, 16><<<cus, 1024, lds, st>>>((const uint8_t*)W, s, V, K, x, logits, argmax,        \
+                                                               counter, best);                                      \
+    return hipGetLastError();                                                                                       \
+  }
+      WSX_WT(2) WSX_WT(3) WSX_WT(4)
+#undef WSX_WT
+    }
   }
   if (T >= 2 && !norm && wt == W_FP8 && K == 2560 && (size_t)V * K < ((size_t)1 << 31)) {
     // the matrix-core head for the verify pass's rows (one workgroup per CU, at most kHeadMaxGrid)
