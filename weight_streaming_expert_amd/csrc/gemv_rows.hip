@@ -659,164 +659,6 @@ __global__ void __launch_bounds__(1024) lm_head_wide_kernel(const uint8_t* __res
 }
 
 
-// ---------------------------------------------------------------- LM head, 2-4 tokens, on the matrix cores
-
-// The verify pass's head ([saipien] "Draft three tokens, verify four": the
-// verify pass scores four positions; here one read of the head serves all
-// of them) as a small dense contraction on
-// v_mfma_f32_16x16x32_bf16: 16 head rows x 32 K values x 16 token columns
-// (columns past T are zero).  E4M3 codes are decoded to bf16 exactly; the row
-// scale multiplies the fp32 sum.  Four 256-thread workgroups per CU; the work
-// unit of a wavefront is (16-row tile, quarter of K), and the four wavefronts
-// of a workgroup take the four quarters of one tile (so the tile's 40 KB are
-// read together), their partial tiles meet in LDS and are added in quarter
-// order; the barrier of each tile couples only those four wavefronts.  The MFMA's
-// 32-wide K slice is a permutation of K: lane (r, q) takes the 16-code granule
-// at K offset 64 j + 16 q of its quarter and feeds codes 0-7 and 8-15 to two
-// MFMAs, and the token columns take the same activations from LDS.  Each
-// wavefront keeps its next unit's loads in flight during the current one.
-__device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
-  const bf16x2_t p0 = fp8x2_to_bf16x2<false>(w0), p1 = fp8x2_to_bf16x2<true>(w0);
-  const bf16x2_t p2 = fp8x2_to_bf16x2<false>(w1), p3 = fp8x2_to_bf16x2<true>(w1);
-  bf16x8_t r;
-  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-  return r;
-}
-
-// One unit's codes (lane (r, q): row tile*16 + r) and the row scales of the
-// output rows the lane will hold (tile*16 + 4q .. +3; a buffer load past the
-// end of the scales returns 0), all issued together.
-template <int NS>
-__device__ __forceinline__ void head_unit_load(__amdgpu_buffer_rsrc_t W, __amdgpu_buffer_rsrc_t Sr, int V, int K,
-                                               int unit, uint4 (&w)[NS], float (&sc)[4]) {
-  const int lane = threadIdx.x & 63;
-  const int tile = unit >> 2, quarter = unit & 3;
-  const int row = tile * 16 + (lane & 15), q = lane >> 4;
-  const bool ok = row < V;
-  const uint32_t o = (uint32_t)(ok ? row : 0) * (uint32_t)K + (uint32_t)(quarter * (K / 4) + 16 * q);
-#pragma unroll
-  for (int j = 0; j < NS; ++j)
-    w[j] = ok ? __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(W, o + 64 * j, 0, 2))
-              : make_uint4(0, 0, 0, 0);
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-    sc[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(Sr, (uint32_t)(tile * 16 + 4 * q + r) * 4, 0, 0));
-}
-
-template <int T, int NS>   // NS: 64-value K steps per quarter of K
-__global__ void __launch_bounds__(256) lm_head_mfma_kernel(const uint8_t* __restrict__ W,
-                                                            const float* __restrict__ row_scale, int V, int K,
-                                                            const uint16_t* __restrict__ x, float* __restrict__ logits,
-                                                            int32_t* __restrict__ argmax, unsigned* counter,
-                                                            float* part_v, int* part_i) {
-  constexpr int NW = 4;
-  constexpr int XPT = 5;   // 16-byte activation chunks per thread: T K / 8 <= 256 XPT
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ float wv_[NW][T];
-  __shared__ int wi_[NW][T];
-  __shared__ int flag;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int col = lane & 15, q = lane >> 4;
-  const int KS = K + 8;                                              // bf16 per LDS activation row
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                  // [T][KS]
-  f32x4_t* pt = reinterpret_cast<f32x4_t*>(smem + (((size_t)T * KS * 2 + 15) & ~(size_t)15));   // [2][NW][64]
-  const __amdgpu_buffer_rsrc_t Wr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(W), 0, 0x7FFFFFFF, 0x00020000);
-  const __amdgpu_buffer_rsrc_t Sr =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row_scale), 0, V * 4, 0x00020000);
-  const int units = ((V + 15) / 16) * 4;
-  const int stride = (int)gridDim.x * NW;
-  const int iters = (units + stride - 1) / stride;
-  int u = (int)blockIdx.x * NW + wave;
-  // x first (T*K/8 16-byte chunks, XPT per thread at most), then the first unit
-  uint4 xv[XPT];
-  const int nx = T * K / 8;
-#pragma unroll
-  for (int i = 0; i < XPT; ++i) {
-    const int c = t + 256 * i;
-    xv[i] = c < nx ? ld16(x + 8 * c) : make_uint4(0, 0, 0, 0);
-  }
-  uint4 cw[NS];
-  float cs[4] = {0.f, 0.f, 0.f, 0.f};
-  if (u < units) head_unit_load<NS>(Wr, Sr, V, K, u, cw, cs);
-  issue_here();
-#pragma unroll
-  for (int i = 0; i < XPT; ++i) {
-    const int c = t + 256 * i;
-    if (c < nx) *reinterpret_cast<uint4*>(xs + (c / (K / 8)) * KS + (c % (K / 8)) * 8) = xv[i];
-  }
-  lds_barrier();
-  float bv = -INFINITY;   // this lane's token column `col` (< T), rows of the tiles this wavefront reduces
-  int bi = 0x7FFFFFFF;
-  for (int it = 0; it < iters; ++it) {
-    uint4 nw[NS];
-    float ns[4] = {0.f, 0.f, 0.f, 0.f};
-    const int un = u + stride;
-    if (un < units) head_unit_load<NS>(Wr, Sr, V, K, un, nw, ns);
-    issue_here();
-    f32x4_t d = {0.f, 0.f, 0.f, 0.f};
-    if (u < units) {
-      const int k0 = (u & 3) * (K / 4);
-#pragma unroll
-      for (int j = 0; j < NS; ++j) {
-        uint4 b0 = make_uint4(0, 0, 0, 0), b1 = make_uint4(0, 0, 0, 0);
-        if (col < T) {
-          const uint4* src = reinterpret_cast<const uint4*>(xs + col * KS + k0 + 64 * j + 16 * q);
-          b0 = src[0];
-          b1 = src[1];
-        }
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(cw[j].x, cw[j].y),
-                                                    __builtin_bit_cast(bf16x8_t, b0), d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(cw[j].z, cw[j].w),
-                                                    __builtin_bit_cast(bf16x8_t, b1), d, 0, 0, 0);
-      }
-    }
-    // D: lane (col, q) holds rows 4q .. 4q+3 of the tile for token column col
-    f32x4_t* ptb = pt + (size_t)(it & 1) * NW * 64;
-    ptb[wave * 64 + lane] = d;
-    lds_barrier();
-    if ((wave & 3) == 0 && u < units && col < T) {
-      const f32x4_t a0 = ptb[(wave + 0) * 64 + lane], a1 = ptb[(wave + 1) * 64 + lane];
-      const f32x4_t a2 = ptb[(wave + 2) * 64 + lane], a3 = ptb[(wave + 3) * 64 + lane];
-      const int tile = u >> 2;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = tile * 16 + 4 * q + r;
-        if (row < V) {
-          const float l = (((a0[r] + a1[r]) + a2[r]) + a3[r]) * cs[r];
-          if (logits) logits[(size_t)col * V + row] = l;
-          if (better(l, row, bv, bi)) { bv = l; bi = row; }
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NS; ++j) cw[j] = nw[j];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) cs[r] = ns[r];
-    u = un;
-  }
-  // per token: the lanes of its column (q = 0..3) in this wavefront, then the
-  // workgroup's wavefronts, then the workgroups (the last one to finish)
-#pragma unroll
-  for (int o = 16; o <= 32; o <<= 1) {
-    const float ov = __shfl_xor(bv, o);
-    const int oi = __shfl_xor(bi, o);
-    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-  }
-  if (lane < T) { wv_[wave][lane] = bv; wi_[wave][lane] = bi; }
-  lds_barrier();
-  if (t < T) {
-    float v = wv_[0][t];
-    int i = wi_[0][t];
-    for (int w = 1; w < NW; ++w)
-      if (better(wv_[w][t], wi_[w][t], v, i)) { v = wv_[w][t]; i = wi_[w][t]; }
-    st_dev(part_v + (size_t)blockIdx.x * T + t, v);
-    st_dev(part_i + (size_t)blockIdx.x * T + t, i);
-  }
-  if (!last_block_arrived(counter, gridDim.x, &flag)) return;
-  head_partials_argmax<T>(part_v, part_i, (int)gridDim.x, wv_, wi_, argmax);
-}
-
 // ---------------------------------------------------------------- router + top-k
 
 // Top-k of one token's E logits (E <= 4 * 256) by the whole 256-thread
@@ -1566,24 +1408,6 @@ hipError_t launch_lm_head(int wt, const void* W, const float* s, int V, int K, c
   }
       WSX_WT(2) WSX_WT(3) WSX_WT(4)
 #undef WSX_WT
-    }
-  }
-  if (T >= 2 && !norm && wt == W_FP8 && K == 2560 && (size_t)V * K < ((size_t)1 << 31)) {
-    // the matrix-core head for the verify pass's rows (one workgroup per CU, at most kHeadMaxGrid)
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus >= 1) {
-      const int grid = 4 * cus < kHeadMaxGrid ? 4 * cus : kHeadMaxGrid;   // four 256-thread workgroups per CU
-      float* pv = reinterpret_cast<float*>((char*)ws + 256);
-      int* pi = reinterpret_cast<int*>((char*)ws + 256 + (size_t)kHeadMaxGrid * WSX_MAX_T * 4);
-      const size_t lds = (((size_t)T * (K + 8) * 2 + 15) & ~(size_t)15) + (size_t)2 * 4 * 64 * 16;
-#define WSX_MF(TV) \
-  if (T == TV) { \
-    lm_head_mfma_kernel<TV, 10><<<grid, 256, lds, st>>>((const uint8_t*)W, s, V, K, x, logits, argmax, counter, pv, pi); \
-    return hipGetLastError(); \
-  }
-      WSX_MF(2) WSX_MF(3) WSX_MF(4)
-#undef WSX_MF
     }
   }
   const int grid = head_grid(V);
