@@ -14,15 +14,15 @@ afterwards.
 
 Prints one JSON line (rank 0) with the µs per step, the achieved HBM rate of
 the step's algorithmic bytes, the roofline object of the dominant kernel (the
-single-launch decode step), the standalone FP8 head kernel's rate, a
-per-component breakdown (one MoE layer over 100 seeded cold inputs, the FP8
-and BF16 heads, the 4-token verify pass, the sampling epilogue at the GSM8K
-settings, the load-time quantizer, the W4A8 layer at 1 and 4 tokens, the
-grouped layer at 16 tokens in bf16 and W4A8), a
-pure-read bandwidth probe, and the
-CPU oracle on three of the timed steps (every layer checked against the
-device, teacher-forced) with its time per step at one BLAS thread and at all
-cores, plus its time per unit of the smaller workloads.
+single-launch decode step), the standalone FP8 head kernel's rate, the 4-token
+verify pass through all layers and the head, a per-component breakdown (one
+MoE layer over 100 seeded cold inputs at 1 and 4 tokens, the FP8 and BF16
+heads, the sampling epilogue at the GSM8K settings, the load-time quantizer,
+the W4A8 layer at 1 and 4 tokens, the grouped layer at 16 tokens in bf16 and
+W4A8), a pure-read bandwidth probe, and the CPU oracle on three of the timed
+steps (every layer checked against the device, teacher-forced) with its time
+per step at one BLAS thread and at all cores, plus its time per unit of the
+smaller workloads.
 """
 
 import argparse
@@ -196,6 +196,53 @@ def main():
                 "frac_of_read_probe": round(k_gbps / probe["GBps"], 4)}
     log(f"step kernel: {k_us:.1f} us per launch, {k_gbps:.0f} GB/s; read probe {probe['GBps']:.0f} GB/s")
 
+    # ------------------------------------------------------------------ the verify pass through the whole stack
+    # Four resident tokens per step through all layers and the head (the
+    # multi-token-prediction verify shape), ten steps per graph; the last
+    # step's outputs are checked bit for bit against an eager call.
+    n4 = max(1, n_tok // 4)
+    tok4 = tokens.reshape(n_tok, H)[torch.arange(4 * n4, device=dev) % n_tok].reshape(n4, 4, H)
+    ws4 = ops.workspace(ops.decode_step_workspace_bytes(4, H, I, E, k, V), dev)
+    out4 = dict(h=torch.empty((4, H), dtype=torch.bfloat16, device=dev),
+                logits=torch.empty((4, V), dtype=torch.float32, device=dev),
+                argmax=torch.empty((4,), dtype=torch.int32, device=dev))
+    ops.moe_decode_step(tok4[0], stack, head, ws=ws4, out=out4)
+    torch.cuda.synchronize()
+    g4 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g4):
+        for j in range(10):
+            ops.moe_decode_step(tok4[j % n4], stack, head, ws=ws4, out=out4)
+    g4.replay()
+    torch.cuda.synchronize()
+    v_reps = 5
+    e0.record()
+    for _ in range(v_reps):
+        g4.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    v_us = e0.elapsed_time(e1) * 1e3 / (10 * v_reps)
+    g_h, g_am = out4["h"].clone(), out4["argmax"].clone()
+    ops.moe_decode_step(tok4[9 % n4], stack, head, ws=ws4, out=out4)
+    torch.cuda.synchronize()
+    v_ok = bool(torch.equal(g_h, out4["h"]) and torch.equal(g_am, out4["argmax"]))
+    # algorithmic bytes of each of the ten steps: every layer's distinct
+    # routed experts (from a traced eager call) + shared expert + router, and
+    # the head
+    v_bytes = []
+    for j in range(10):
+        ids = ops.moe_decode_step(tok4[j % n4], stack, head, ws=ws4, trace=True)["ids_trace"].cpu().numpy()
+        v_bytes.append(sum(configs.moe_layer_bytes(m, len(np.unique(ids[l]))) for l in range(L))
+                       + configs.head_bytes(V, H, 4, True))
+    v_gbps = float(np.mean(v_bytes)) / (v_us * 1e-6) / 1e9
+    verify_step = {"tokens_per_step": 4, "us_per_step": round(v_us, 2), "over_one_token_step": round(v_us / k_us, 3),
+                   "bytes_per_step": int(np.mean(v_bytes)), "achieved_GBps": round(v_gbps, 1),
+                   "frac_of_peak": round(v_gbps / PEAK_GBPS, 4), "graph_equals_eager": v_ok,
+                   "note": "4 seeded resident tokens per step through all layers (per-phase launches) and the FP8 "
+                           "head with argmax; ten steps per graph, warm replays"}
+    log(f"verify step (4 tokens): {v_us:.1f} us ({v_us / k_us:.2f}x the one-token step), {v_gbps:.0f} GB/s, "
+        f"graph == eager: {v_ok}")
+    del ws4
+
     # ------------------------------------------------------------------ the FP8 LM head kernel on its own
     u = torch.from_numpy(inputs.activations(wl, 0).view(np.int16)).view(torch.bfloat16).to(dev)
     hws = ops.workspace(ops.lm_head_workspace_bytes(1, V, H), dev)
@@ -243,6 +290,7 @@ def main():
                                 "differ_from_eager": int(np.sum(timed_am != eager_am))},
         "roofline": roofline,
         "head_kernel": head_kernel,
+        "verify_step": verify_step,
         "read_probe": probe,
     }
 
