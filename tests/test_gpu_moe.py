@@ -129,6 +129,58 @@ def test_one_token_handmade_lists_and_workspace_reuse(ops, tiny):
         P.check_residual(res, y, h)
 
 
+@pytest.mark.parametrize("shape", ["tiny", "ling"])
+def test_four_tokens_handmade_lists_and_workspace_reuse(ops, tiny, ling, shape):
+    """Four tokens with caller-built expert-sorted token lists (one launch for
+    gate/up and down, whose slot counters must be back at zero after every
+    call): one workspace serves lists with shared and unshared slots, an
+    out-of-range id (which contributes nothing), a full list and an empty
+    one, with and without the shared expert, each checked against the oracle
+    and against the same call on a fresh workspace, bit for bit."""
+    wl, lw, dw = tiny if shape == "tiny" else ling
+    m = wl.moe
+    T = 4
+    dev = torch.device("cuda:0")
+    ws = ops.workspace(ops.moe_workspace_bytes(T, m.H, m.I, m.E, m.k), dev)
+    get = lambda e: (lw["w13c"][e], lw["w13s"][e], lw["w2c"][e], lw["w2s"][e])
+    rng = np.random.default_rng(17)
+    full = sorted(rng.choice(m.E, size=T * m.k, replace=False).tolist())
+    cases = (
+        [(1, {0: 0.5, 1: 0.25}), (4, {2: 1.0}), (7, {0: 0.5, 3: 0.75}), (12, {1: 0.25, 2: 0.5}), (m.E + 5, {1: 0.5})],
+        [],
+        [(e, {t: 1.0 / m.k for t in range(T) if (i + t) % T == 0 or m.k > 2}) for i, e in enumerate(full)],
+        [(0, {0: 1.0, 1: 1.0, 2: 1.0, 3: 1.0})],
+    )
+    for i, case in enumerate(cases * 2):
+        shared = dw["shared"] if i % 3 != 1 else None
+        x = inputs.normal_bf16((4, 2, i), (T, m.H), 1.0)
+        res = inputs.normal_bf16((4, 3, i), (T, m.H), 1.0)
+        el = np.zeros(1 + T * m.k, dtype=np.int32)
+        el[0] = len(case)
+        sw = np.zeros((T * m.k, T), dtype=np.float32)
+        for s, (e, tw) in enumerate(case):
+            el[1 + s] = e
+            for t, wt in tw.items():
+                sw[s, t] = wt
+        args = (P.to_dev_bf16(x), dw["w13c"], dw["w13s"], dw["w2c"], dw["w2s"], P.to_dev(el), P.to_dev(sw), m.k)
+        y, h = ops.moe_expert_gemv_mxfp4(*args, shared=shared, residual=P.to_dev_bf16(res), ws=ws)
+        y1, h1 = ops.moe_expert_gemv_mxfp4(*args, shared=shared, residual=P.to_dev_bf16(res))
+        y, h, y1, h1 = P.np_(y), P.bits(h), P.np_(y1), P.bits(h1)
+        assert np.array_equal(y, y1) and np.array_equal(h, h1), (shape, i)
+        valid = [s for s, (e, _) in enumerate(case) if 0 <= e < m.E]
+        d = [OM.down(OM.gate_up(x, *get(case[s][0])[:2], m.I), *get(case[s][0])[2:]) for s in valid]
+        d = np.stack(d) if d else np.zeros((0, T, m.H))
+        sh = lw["shared"]
+        d_sh = OM.down(OM.gate_up(x, sh[0], sh[1], m.I), sh[2], sh[3]) if shared is not None else None
+        y_ref = OM.combine(d, sw[valid].astype(np.float64).reshape(len(valid), T), d_sh)
+        if not valid and shared is None:
+            assert np.array_equal(y, np.zeros_like(y)), (shape, i)
+        else:
+            ok, worst = C.fp_close(y, y_ref)
+            assert ok, (shape, i, worst)
+        P.check_residual(res, y, h)
+
+
 def test_router_ties_resolve_to_lowest_id(ops):
     H, E, k = 256, 64, 8
     w = inputs.normal_f32((4,), (E, H), 0.02)
