@@ -47,7 +47,73 @@ template <int T, int NT>
 __device__ __forceinline__ void stage_input(const uint16_t* __restrict__ x, int K, bool norm, uint16_t* u_out,
                                             uint16_t* xs, float* red) {
   const int tid = threadIdx.x;
-  stage_to_lds<NT, (T * 320 + NT - 1) / NT>(x, xs, T * K / 8);
+  constexpr int MAXC = (T * 320 + NT - 1) / NT;
+  if (norm && T * K / 8 <= MAXC * NT) {
+    // every chunk stays in this thread's registers: the sums of squares come
+    // from them (each chunk's 8 values in order, then the thread's chunks of
+    // a token in order, the wavefront tree and the wavefronts in order), and
+    // the normalized chunk goes to LDS (and u_out) in one 16-byte store
+    const int cpt = K / 8;   // chunks per token
+    uint4 v[MAXC];
+#pragma unroll
+    for (int j = 0; j < MAXC; ++j) {
+      const int i = tid + j * NT;
+      v[j] = i < T * cpt ? ld16(x + (size_t)i * 8) : make_uint4(0, 0, 0, 0);
+    }
+    float ss[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) ss[t] = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXC; ++j) {
+      const int i = tid + j * NT;
+      const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+      float c = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float a = bf16_bits_to_f32(w[q] & 0xFFFFu), b = bf16_bits_to_f32(w[q] >> 16);
+        c = fmaf(a, a, c);
+        c = fmaf(b, b, c);
+      }
+      const int tok = i / cpt;
+#pragma unroll
+      for (int t = 0; t < T; ++t) ss[t] += (t == tok) ? c : 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const float w = wave_sum(ss[t]);
+      if ((tid & 63) == 0) red[t * (NT / 64) + (tid >> 6)] = w;
+    }
+    __syncthreads();
+    float r[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      float sq = 0.f;
+      for (int w = 0; w < NT / 64; ++w) sq += red[t * (NT / 64) + w];
+      r[t] = 1.0f / sqrtf(sq / (float)K + 1e-6f);
+    }
+#pragma unroll
+    for (int j = 0; j < MAXC; ++j) {
+      const int i = tid + j * NT;
+      if (i < T * cpt) {
+        const int tok = i / cpt;
+        float rt = r[0];
+#pragma unroll
+        for (int t = 1; t < T; ++t) rt = (t == tok) ? r[t] : rt;
+        const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+        uint32_t o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          o[q] = f32_to_bf16_rne(bf16_bits_to_f32(w[q] & 0xFFFFu) * rt) |
+                 (f32_to_bf16_rne(bf16_bits_to_f32(w[q] >> 16) * rt) << 16);
+        const uint4 u = make_uint4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<uint4*>(xs + (size_t)i * 8) = u;
+        if (blockIdx.x == 0 && u_out) *reinterpret_cast<uint4*>(u_out + (size_t)i * 8) = u;
+      }
+    }
+    __syncthreads();
+    return;
+  }
+  stage_to_lds<NT, MAXC>(x, xs, T * K / 8);
   if (!norm) { __syncthreads(); return; }
   __syncthreads();
 #pragma unroll
@@ -303,11 +369,17 @@ __device__ __forceinline__ void head_group_load(__amdgpu_buffer_rsrc_t W, const 
 // token the products are added in exactly the 1-token kernel's order, so each
 // token's logits equal the 1-token head's bit for bit.  Per token, every
 // workgroup joins its best (value, row) to a 64-bit atomic max, and the last
-// workgroup publishes the argmaxes.
+// workgroup publishes the argmaxes.  With `norm` the rows are first RMS-
+// normalized (u = RNE_bf16(x / sqrt(mean(x^2) + 1e-6)), the decode step's
+// final norm): each token's sum of squares is formed from the staged
+// registers in one fixed order (a chunk's 8 values, the thread's chunks, the
+// wavefront tree, then the 16 wavefronts in order), so every workgroup
+// derives the same u; the first workgroup also writes u to u_out.
 template <int TT, int GPL, int RL>
 __global__ void __launch_bounds__(1024) lm_head_wide_t_kernel(const uint8_t* __restrict__ W,
                                                               const float* __restrict__ row_scale, int V, int K,
-                                                              const uint16_t* __restrict__ x, float* __restrict__ logits,
+                                                              const uint16_t* __restrict__ x, int norm,
+                                                              uint16_t* __restrict__ u_out, float* __restrict__ logits,
                                                               int32_t* __restrict__ argmax, unsigned* counter,
                                                               unsigned long long* best) {
   constexpr int RPW = 64 / RL, NW = 16, GS = 48;   // LayHead: 16 bf16 in 48 bytes per granule
@@ -334,6 +406,58 @@ __global__ void __launch_bounds__(1024) lm_head_wide_t_kernel(const uint8_t* __r
   HeadGroup<W_FP8, GPL, RL> cur;
   if (grp >= 0) head_group_load<W_FP8, GPL, RL>(Wr, row_scale, V, G, row_bytes, grp, cur);
   issue_here();
+  if (norm) {
+    __shared__ float sq[TT][NW];
+    float ss[TT];
+#pragma unroll
+    for (int k2 = 0; k2 < TT; ++k2) ss[k2] = 0.f;
+#pragma unroll
+    for (int q = 0; q < XC; ++q) {
+      const int i = t + 1024 * q;
+      const uint32_t w[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
+      float c2 = 0.f;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float a = bf16_bits_to_f32(w[h] & 0xFFFFu), b = bf16_bits_to_f32(w[h] >> 16);
+        c2 = fmaf(a, a, c2);
+        c2 = fmaf(b, b, c2);
+      }
+      const int tok = i < TT * nx ? i / nx : -1;
+#pragma unroll
+      for (int k2 = 0; k2 < TT; ++k2) ss[k2] += (k2 == tok) ? c2 : 0.f;
+    }
+#pragma unroll
+    for (int k2 = 0; k2 < TT; ++k2) {
+      const float w = wave_sum(ss[k2]);
+      if (lane == 0) sq[k2][wave] = w;
+    }
+    lds_barrier();
+    float r[TT];
+#pragma unroll
+    for (int k2 = 0; k2 < TT; ++k2) {
+      float a = 0.f;
+      for (int w = 0; w < NW; ++w) a += sq[k2][w];
+      r[k2] = 1.0f / sqrtf(a / (float)K + 1e-6f);
+    }
+#pragma unroll
+    for (int q = 0; q < XC; ++q) {
+      const int i = t + 1024 * q;
+      if (i < TT * nx) {
+        const int tok = i / nx;
+        float rt = r[0];
+#pragma unroll
+        for (int k2 = 1; k2 < TT; ++k2) rt = (k2 == tok) ? r[k2] : rt;
+        const uint32_t w[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
+        uint32_t o[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          o[h] = f32_to_bf16_rne(bf16_bits_to_f32(w[h] & 0xFFFFu) * rt) |
+                 (f32_to_bf16_rne(bf16_bits_to_f32(w[h] >> 16) * rt) << 16);
+        xv[q] = make_uint4(o[0], o[1], o[2], o[3]);
+        if (blockIdx.x == 0 && u_out) *reinterpret_cast<uint4*>(u_out + 8 * (size_t)i) = xv[q];
+      }
+    }
+  }
 #pragma unroll
   for (int q = 0; q < XC; ++q) {
     const int i = t + 1024 * q;
@@ -1389,7 +1513,7 @@ hipError_t launch_lm_head(int wt, const void* W, const float* s, int V, int K, c
                                           reinterpret_cast<unsigned long long*>((char*)ws + 64), st, &done);
     if (done || e != hipSuccess) return e;
   }
-  if (T >= 2 && !norm && wt == W_FP8 && (K == 2560 || K == 256) && (size_t)V * K < ((size_t)1 << 31)) {
+  if (T >= 2 && wt == W_FP8 && (K == 2560 || K == 256) && (size_t)V * K < ((size_t)1 << 31)) {
     // the wide head for the verify pass's rows: one 1024-thread workgroup per CU
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
@@ -1399,11 +1523,11 @@ hipError_t launch_lm_head(int wt, const void* W, const float* s, int V, int K, c
 #define WSX_WT(TV)                                                                                                  \
   if (T == TV) {                                                                                                    \
     if (K == 2560)                                                                                                  \
-      lm_head_wide_t_kernel<TV, 10, 16><<<cus, 1024, lds, st>>>((const uint8_t*)W, s, V, K, x, logits, argmax,       \
-                                                                counter, best);                                     \
+      lm_head_wide_t_kernel<TV, 10, 16><<<cus, 1024, lds, st>>>((const uint8_t*)W, s, V, K, x, norm, u_out, logits,  \
+                                                                argmax, counter, best);                             \
     else                                                                                                            \
-      lm_head_wide_t_kernel<TV, 1, 16><<<cus, 1024, lds, st>>>((const uint8_t*)W, s, V, K, x, logits, argmax,        \
-                                                               counter, best);                                      \
+      lm_head_wide_t_kernel<TV, 1, 16><<<cus, 1024, lds, st>>>((const uint8_t*)W, s, V, K, x, norm, u_out, logits,   \
+                                                               argmax, counter, best);                              \
     return hipGetLastError();                                                                                       \
   }
       WSX_WT(2) WSX_WT(3) WSX_WT(4)
