@@ -722,6 +722,56 @@ __global__ void __launch_bounds__(256) moe_down1_kernel(int H, int I, int E, int
 // so the result never depends on timing.
 constexpr int kDnRows = 32;
 
+// The products of one pass of the kernel below for its first TCX tokens
+// (TCX <= 2): lane (kg, rq) over rows n0 + 4 rq .. +3 and MX blocks kg,
+// kg + 8, ..., each token's sum in block, then element order.
+template <int NKB, int TCX>
+__device__ __forceinline__ void down_token_dots(const uint4 (&cw)[NKB][4], const uint8_t* ls, const float* aw,
+                                                int lstride, int kg, int rq, int NB, float (&acc)[4][2]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int j = 0; j < TCX; ++j) acc[r][j] = 0.f;
+#pragma unroll
+  for (int b = 0; b < NKB; ++b) {
+    const int kb = kg + 8 * b;
+    if (kb >= NB) continue;
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      float av[TCX][8];
+#pragma unroll
+      for (int j = 0; j < TCX; ++j) {
+        const float4* ap = reinterpret_cast<const float4*>(aw + j * lstride + kb * 36 + c4 * 8);
+        const float4 v0 = ap[0], v1 = ap[1];
+        av[j][0] = v0.x; av[j][1] = v0.y; av[j][2] = v0.z; av[j][3] = v0.w;
+        av[j][4] = v1.x; av[j][5] = v1.y; av[j][6] = v1.z; av[j][7] = v1.w;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t wd = c4 == 0 ? cw[b][r].x : c4 == 1 ? cw[b][r].y : c4 == 2 ? cw[b][r].z : cw[b][r].w;
+        const float sc = e8m0_to_f32(ls[(4 * rq + r) * NB + kb]);
+        const f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc, 0);
+        const f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc, 1);
+        const f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc, 2);
+        const f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc, 3);
+#pragma unroll
+        for (int j = 0; j < TCX; ++j) {
+          float v = acc[r][j];
+          v = fmaf(p0.x, av[j][0], v);
+          v = fmaf(p0.y, av[j][1], v);
+          v = fmaf(p1.x, av[j][2], v);
+          v = fmaf(p1.y, av[j][3], v);
+          v = fmaf(p2.x, av[j][4], v);
+          v = fmaf(p2.y, av[j][5], v);
+          v = fmaf(p3.x, av[j][6], v);
+          v = fmaf(p3.y, av[j][7], v);
+          acc[r][j] = v;
+        }
+      }
+    }
+  }
+}
+
 __device__ __forceinline__ int dpos(int i) { return (i >> 5) * 36 + (i & 31); }
 
 int down_sparse_groups(int T, int k) { return (T * k + (T + 3) / 4 + 3) / 4; }
@@ -829,53 +879,21 @@ __global__ void __launch_bounds__(256) moe_down_sparse_kernel(
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // a pass with one token (most routed slots of a verify pass) takes
+      // only that token's products
       float acc[4][TC];
+      if (tok[1] >= 0) {
+        down_token_dots<NKB, 2>(cw, ls, aw, lstride, kg, rq, NB, acc);
+      } else {
+        down_token_dots<NKB, 1>(cw, ls, aw, lstride, kg, rq, NB, acc);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int j = 0; j < TC; ++j) acc[r][j] = 0.f;
-#pragma unroll
-      for (int b = 0; b < NKB; ++b) {
-        const int kb = kg + 8 * b;
-        if (kb >= NB) continue;
-#pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-          float av[TC][8];
-#pragma unroll
-          for (int j = 0; j < TC; ++j) {
-            const float4* ap = reinterpret_cast<const float4*>(aw + j * lstride + kb * 36 + c4 * 8);
-            const float4 v0 = ap[0], v1 = ap[1];
-            av[j][0] = v0.x; av[j][1] = v0.y; av[j][2] = v0.z; av[j][3] = v0.w;
-            av[j][4] = v1.x; av[j][5] = v1.y; av[j][6] = v1.z; av[j][7] = v1.w;
-          }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const uint32_t wd = c4 == 0 ? cw[b][r].x : c4 == 1 ? cw[b][r].y : c4 == 2 ? cw[b][r].z : cw[b][r].w;
-            const float sc = kb < NB ? e8m0_to_f32(ls[(4 * rq + r) * NB + kb]) : 0.f;
-            const f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc, 0);
-            const f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc, 1);
-            const f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc, 2);
-            const f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc, 3);
-#pragma unroll
-            for (int j = 0; j < TC; ++j) {
-              float v = acc[r][j];
-              v = fmaf(p0.x, av[j][0], v);
-              v = fmaf(p0.y, av[j][1], v);
-              v = fmaf(p1.x, av[j][2], v);
-              v = fmaf(p1.y, av[j][3], v);
-              v = fmaf(p2.x, av[j][4], v);
-              v = fmaf(p2.y, av[j][5], v);
-              v = fmaf(p3.x, av[j][6], v);
-              v = fmaf(p3.y, av[j][7], v);
-              acc[r][j] = v;
-            }
-          }
-        }
+        for (int r = 0; r < 4; ++r) acc[r][1] = 0.f;
       }
       // weighted row sums (fixed DPP tree over the 8 lanes of a row group);
       // each (token, row) of this slot is written by one lane
 #pragma unroll
       for (int j = 0; j < TC; ++j) {
+        if (tok[j] < 0) continue;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float v = sum8(acc[r][j] * wt[j]);
