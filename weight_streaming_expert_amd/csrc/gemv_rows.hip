@@ -1058,6 +1058,7 @@ __global__ void __launch_bounds__(256) router_topk_kernel(
   __shared__ int sel_id[WSX_MAX_T * WSX_MAX_K];
   __shared__ float sel_w[WSX_MAX_T * WSX_MAX_K];
   __shared__ float sw_tab[WSX_MAX_T * WSX_MAX_K * WSX_MAX_T];
+  __shared__ unsigned bm[WSX_MAX_E / 32];   // bitmap of the selected ids
   const float* rv_t;
   const int* rid_t;
   int t = 0, j0 = -1;
@@ -1096,24 +1097,41 @@ __global__ void __launch_bounds__(256) router_topk_kernel(
   __syncthreads();
   const int n = T * k;
   if (wave == 0) {
-    // lane j < n holds selection j (token j / k); the distinct ids and their
-    // ascending slots come from registers: readlane broadcasts, a ballot of
-    // the first occurrences, and a count of the smaller distinct ids
-    constexpr int NS = WSX_MAX_T * WSX_MAX_K;   // n <= NS <= 64
-    const int id = (lane < n) ? sel_id[lane] : 0x7FFFFFFF;
-    int first = lane < n;
-#pragma unroll
-    for (int j = 0; j < NS; ++j)
-      if (j < lane && __builtin_amdgcn_readlane(id, j) == id) first = 0;
-    const unsigned long long fm = __ballot(first);
-    int rank = 0;
-#pragma unroll
-    for (int j = 0; j < NS; ++j) rank += (int)(((fm >> j) & 1ull) != 0 && __builtin_amdgcn_readlane(id, j) < id);
-    if (lane == 0) expert_list[0] = __popcll(fm);
-    if (lane < n && first) expert_list[1 + rank] = id;
-    // the zeros are stored before the weights (one wavefront, in order)
+    // lane j < n holds selection j (token j / k).  The selected ids go into a
+    // bitmap; an id's slot is the number of selected ids below it (the
+    // popcounts of the words before its own, by a prefix over the lanes, plus
+    // the bits below it in its word), so every selection of an id writes the
+    // same list entry.  One wavefront does it all: its LDS accesses complete
+    // in order, so only the compiler has to keep them in order.
+    const int nw = (E + 31) / 32;   // <= 32 words
+    // (clamped: a selection is always an id below E, but the bitmap must never be indexed past its end)
+    const int id = lane < n ? min(max(sel_id[lane], 0), E - 1) : 0;
+    if (lane < nw) bm[lane] = 0u;
     for (int e = lane; e < n * T; e += 64) sw_tab[e] = 0.f;
-    if (lane < n) sw_tab[rank * T + lane / k] = sel_w[lane];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (lane < n) atomicOr(&bm[id >> 5], 1u << (id & 31));
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const unsigned word = lane < nw ? bm[lane] : 0u;
+    const int c = __popc(word);
+    int incl = c;
+#pragma unroll
+    for (int d = 1; d < 32; d <<= 1) {
+      const int o = __shfl_up(incl, d);
+      if (lane >= d) incl += o;
+    }
+    const int pre = incl - c;   // selected ids below word `lane`
+    const int w = id >> 5;
+    const int rank = __shfl(pre, w) + __popc(__shfl(word, w) & ((1u << (id & 31)) - 1u));
+    const int total = __shfl(incl, 31);   // (every lane takes part in the shuffle)
+    if (lane == 0) expert_list[0] = total;
+    if (lane < n) {
+      expert_list[1 + rank] = id;
+      sw_tab[rank * T + lane / k] = sel_w[lane];   // a token's k ids are distinct: one entry per (slot, token)
+    }
   }
   __syncthreads();
   for (int e = threadIdx.x; e < n * T; e += 256) slot_w[e] = sw_tab[e];
