@@ -474,9 +474,11 @@ const char* wsx_status_string(wsx_status s) {
 #define WSX_STR(x) WSX_STR2(x)
 const char* wsx_build_info(void) {
   return "libwsx arch=gfx950 hip=" WSX_STR(HIP_VERSION_MAJOR) "." WSX_STR(HIP_VERSION_MINOR)
-         " kernels=decode_step<T1;one-launch;aot:Ling-bf16,tiny-f32;hiprtc:other-shapes>,router_topk<bf16|f32,T1-4;rank-count>,"
-         "moe_gateup<T1;valu-dot2|T2-4;mfma-bf16>,moe_down<T1;valu|T2-4;grouped>,"
-         "lm_head<fp8|bf16,T1;wide-per-CU>,lm_head<fp8,T2-4;mfma-bf16>,lm_head<bf16,T2-4>,quant_fp8,sample<topk<=64,topp>";
+         " kernels=decode_step<T1;one-launch;aot:Ling-bf16,tiny-f32;hiprtc:other-shapes>,"
+         "router_topk<bf16|f32,T1-4;rank-count|T5-16;grouped>,moe_gateup<T1;valu-dot2|T2-4;mfma-bf16|T5-16;mfma-4tiles>,"
+         "moe_down<T1;valu|T2-16;token-lists>,moe_w4a8<T1-16;mfma-scale-f8f6f4>,"
+         "lm_head<fp8|bf16,T1;wide-per-CU>,lm_head<fp8,T2-4;wide-per-CU,norm>,lm_head<bf16,T2-4>,quant_fp8,"
+         "sample<topk<=64,topp;fused-into-head-T1>";
 }
 
 }  // extern "C"

@@ -18,6 +18,8 @@
 // within each 16-lane row, identical for every row, so equal rows give
 // bit-identical logits and ties resolve exactly to the lower index.
 #include "sample_device.h"
+#include <atomic>
+
 #include "wsx_internal.h"
 
 namespace wsx {
@@ -1430,6 +1432,26 @@ int head_grid(int V) {
   return g < 1 ? 1 : (g > kHeadMaxGrid ? kHeadMaxGrid : g);
 }
 
+// The current device's CU count (the wide heads launch one workgroup per
+// CU), queried once per device and kept.
+static hipError_t device_cus(int* cus) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cached[kMaxDev];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  int c = cached[dev].load(std::memory_order_relaxed);
+  if (c < 1) {
+    e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (c < 1) return hipErrorInvalidDevice;
+    cached[dev].store(c, std::memory_order_relaxed);
+  }
+  *cus = c;
+  return hipSuccess;
+}
+
 // The wide 1-token head for the shapes it is compiled for: one workgroup per
 // CU; weights addressed with 32-bit offsets, so the head must be below 2 GiB.
 // smp non-null: the sampling variant (FP8 only; see head_sample_fused_fits).
@@ -1438,10 +1460,9 @@ static hipError_t launch_head_wide(int wt, const void* W, const float* s, int V,
                                    hipStream_t st, bool* done, const HeadSample* smp = nullptr) {
   *done = false;
   if ((size_t)V * K * (wt == W_FP8 ? 1 : 2) >= ((size_t)1 << 31)) return hipSuccess;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus < 1)
-    return hipSuccess;
+  int cus = 0;
+  const hipError_t ce = device_cus(&cus);
+  if (ce != hipSuccess) return ce;
   const int epg = wt == W_FP8 ? 16 : 8, gs = wt == W_FP8 ? 48 : 16;
   const size_t lds = (size_t)(K / epg) * gs;
 #define WSX_WIDE(WTV, GPLV, RLV)                                                                                   \
@@ -1493,9 +1514,8 @@ bool head_sample_fused_fits(int V, int K, int top_k, int cus) {
 }
 
 int head_sample_fused_path(int V, int K, int top_k) {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
+  int cus = 0;
+  if (device_cus(&cus) != hipSuccess) return 0;
   return head_sample_fused_fits(V, K, top_k, cus) ? 1 : 0;
 }
 
@@ -1505,9 +1525,9 @@ hipError_t launch_lm_head_sample_fused(const void* W, const float* s, int V, int
                                        void* head_ws, void* sample_ws, hipStream_t st, bool* done) {
   *done = false;
   if (!head_sample_fused_path(V, K, top_k)) return hipSuccess;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return hipSuccess;
+  int cus = 0;
+  const hipError_t ce = device_cus(&cus);
+  if (ce != hipSuccess) return ce;
   HeadSample smp;
   smp.chunk_max = reinterpret_cast<RankKey*>(sample_ws);
   smp.wg_max = smp.chunk_max + (size_t)cus * 16;
@@ -1533,9 +1553,10 @@ hipError_t launch_lm_head(int wt, const void* W, const float* s, int V, int K, c
   }
   if (T >= 2 && wt == W_FP8 && (K == 2560 || K == 256) && (size_t)V * K < ((size_t)1 << 31)) {
     // the wide head for the verify pass's rows: one 1024-thread workgroup per CU
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus >= 1) {
+    int cus = 0;
+    const hipError_t ce = device_cus(&cus);
+    if (ce != hipSuccess) return ce;
+    {
       unsigned long long* best = reinterpret_cast<unsigned long long*>((char*)ws + 64);   // T words
       const size_t lds = (size_t)T * (K / 16) * 48;
 #define WSX_WT(TV)                                                                                                  \
