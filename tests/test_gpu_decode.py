@@ -51,7 +51,7 @@ def check_step(wl, layers, out, head_q, head_s, h0):
     return P.check_head(head_q, head_s, ut[L], P.np_(out["logits"]), P.np_(out["argmax"]))
 
 
-@pytest.mark.parametrize("T", [1, 4])
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
 def test_tiny_stack_decode_step(ops, T):
     wl = configs.TINY
     L = 3
@@ -79,7 +79,7 @@ def ling_stack(ops):
     return wl, layers, stack, head, P.np_(head.q), P.np_(head.s)
 
 
-@pytest.mark.parametrize("T", [1, 4])
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
 def test_ling_shape_stack_decode_step(ops, ling_stack, T):
     wl, layers, stack, head, qh, sh = ling_stack
     for step in range(2):
