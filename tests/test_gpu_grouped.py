@@ -128,3 +128,14 @@ def test_grouped_w4a8_ling_layer(ops, ling, T):
     x = inputs.normal_bf16((wl.seed, 88, T), (T, wl.moe.H), 1.0)
     res = inputs.normal_bf16((wl.seed, 89, T), (T, wl.moe.H), 1.0)
     check_w4a8(wl, lw, x, res, *run_w4a8(ops, wl, dw, x, res))
+
+
+@pytest.mark.parametrize("T", [5, 13, 16])
+def test_grouped_w4a8_tiny_layer(ops, tiny, T):
+    """Above four tokens the W4A8 layer quantizes its input rows once, ahead of
+    the gate/up workgroups: ragged token counts at the tiny shape."""
+    wl, lw, dw = tiny
+    for step in range(2):
+        x = inputs.normal_bf16((wl.seed, 91, step, T), (T, wl.moe.H), 1.0)
+        res = inputs.normal_bf16((wl.seed, 92, step, T), (T, wl.moe.H), 1.0)
+        check_w4a8(wl, lw, x, res, *run_w4a8(ops, wl, dw, x, res))

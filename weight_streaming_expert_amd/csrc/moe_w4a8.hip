@@ -20,7 +20,9 @@
 //   D (16 x 16, fp32):       lane (col c, group g) holds rows 4g..4g+3.
 // The columns are tokens (T <= 16); columns past T are zero.
 //
-// Two launches per layer, driven by the device-side expert list:
+// Two launches per layer, driven by the device-side expert list (above 4
+// tokens a third one first quantizes the T input rows once, and the gate/up
+// workgroups copy those bytes instead of quantizing):
 //   gate/up  grid (I/32, T*k+1): workgroup (tile, slot) quantizes the T input
 //            rows into LDS, its four wavefronts take 16 gate rows, 16 more
 //            gate rows and the two matching sets of 16 up rows, and it writes
@@ -142,7 +144,8 @@ template <int NS>   // matrix-core steps of 128 covering H
 __global__ void __launch_bounds__(256) moe_gateup_w4a8_kernel(
     const uint16_t* __restrict__ x, int T, int H, int I, int E, int max_slots, const uint8_t* __restrict__ w13c,
     const uint8_t* __restrict__ w13s, const uint8_t* __restrict__ sh13c, const uint8_t* __restrict__ sh13s,
-    const int32_t* __restrict__ el, uint8_t* __restrict__ aq, uint8_t* __restrict__ aqs, float* __restrict__ act) {
+    const int32_t* __restrict__ el, uint8_t* __restrict__ aq, uint8_t* __restrict__ aqs, float* __restrict__ act,
+    const uint8_t* __restrict__ xin) {
   const int slot = blockIdx.y;
   int n_active = el[0];
   n_active = n_active < 0 ? 0 : (n_active > max_slots - 1 ? max_slots - 1 : n_active);
@@ -193,7 +196,26 @@ __global__ void __launch_bounds__(256) moe_gateup_w4a8_kernel(
   extern __shared__ __attribute__((aligned(16))) uint8_t sm[];
   uint8_t* xq = sm;
   uint8_t* xs = sm + (size_t)T * H;
-  for (int b = threadIdx.x; b < T * NB; b += 256) {
+  if (xin) {
+    // quantized once for the layer (the same blocks, the same bytes), laid
+    // out as in LDS: copied with 16-byte loads, four per thread in flight
+    const int nb = T * H + T * NB, n16 = nb / 16;
+    for (int c0 = 0; c0 < n16; c0 += 4 * 256) {
+      uint4 v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = c0 + (int)threadIdx.x + 256 * j;
+        v[j] = c < n16 ? ld16(xin + (size_t)c * 16) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = c0 + (int)threadIdx.x + 256 * j;
+        if (c < n16) *reinterpret_cast<uint4*>(sm + (size_t)c * 16) = v[j];
+      }
+    }
+    for (int i = 16 * n16 + (int)threadIdx.x; i < nb; i += 256) sm[i] = xin[i];
+  }
+  for (int b = xin ? T * NB : (int)threadIdx.x; b < T * NB; b += 256) {
     const int t = b / NB, kb = b - t * NB;
     uint4 in[4];
 #pragma unroll
@@ -401,11 +423,22 @@ hipError_t launch_w4a8_experts(const uint16_t* x, int T, int H, int I, int E, in
   uint8_t* aq = reinterpret_cast<uint8_t*>(abuf);
   uint8_t* aqs = aq + (((size_t)max_slots * T * I + 15) & ~(size_t)15);
   const size_t lds = (size_t)T * H + (size_t)T * (H / 32);
+  // more than 4 tokens: every gate/up workgroup would quantize all T input
+  // rows itself (one dependent round of loads per 256 blocks); quantize them
+  // once instead, into the activation region behind the codes and scales it
+  // holds (fp32-sized, so the bytes fit unless I is tiny against H)
+  const size_t xin_off = (w4a8_act_bytes(T, I, max_slots) + 15) & ~(size_t)15;
+  uint8_t* xin = nullptr;
+  if (T > WSX_MAX_T && xin_off + lds <= (size_t)max_slots * T * I * 4) {
+    xin = aq + xin_off;
+    const hipError_t qe = launch_act_quant(x, T, H, xin, xin + (size_t)T * H, st);
+    if (qe != hipSuccess) return qe;
+  }
   dim3 gg(I / 32, max_slots);
 #define WSX_WG(N)                                                                                              \
   case N:                                                                                                      \
     moe_gateup_w4a8_kernel<N><<<gg, 256, lds, st>>>(x, T, H, I, E, max_slots, w13c, w13s, sh13c, sh13s, el, aq, \
-                                                    aqs, act);                                                 \
+                                                    aqs, act, xin);                                            \
     break;
   switch (steps_case((H + 127) / 128)) {
     WSX_WG(1) WSX_WG(2) WSX_WG(3) WSX_WG(4) WSX_WG(5) WSX_WG(6) WSX_WG(8) WSX_WG(10) WSX_WG(12) WSX_WG(16) WSX_WG(20)
