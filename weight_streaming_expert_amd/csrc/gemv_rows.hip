@@ -17,9 +17,9 @@
 // tokens they are read from LDS.  Row sums are formed by a fixed DPP tree
 // within each 16-lane row, identical for every row, so equal rows give
 // bit-identical logits and ties resolve exactly to the lower index.
-#include "sample_device.h"
 #include <atomic>
 
+#include "sample_device.h"
 #include "wsx_internal.h"
 
 namespace wsx {
