@@ -379,7 +379,7 @@ wsx_status wsx_read_probe(const void* buf, size_t bytes, uint32_t* out, void* st
  * on one GPU shares that GPU's array: calls that overlap on one GPU (different
  * streams, or host threads) race and give unspecified results.
  */
-#define WSX_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+#define WSX_NOALLOC_SCRATCH_BYTES ((size_t)2 << 20)
 wsx_status moe_decode_step_noalloc(const uint16_t* h_in, int T, const wsx_moe_stack* stack,
                                    const uint8_t* head_q, const float* head_scale, int V,
                                    uint16_t* h_out, float* logits, int32_t* argmax,

@@ -172,7 +172,7 @@ def test_noalloc_decode_step_rejects_on_the_host():
     st = _lib.MoeStack(FAKE, 0, FAKE, FAKE, FAKE, FAKE, None, None, None, None, 2, 2560, 768, 512, 8)
     args = lambda **kw: [kw.get("h", FAKE), kw.get("T", 1), ctypes.byref(kw.get("st", st)), FAKE, FAKE,
                          kw.get("V", 157184), FAKE, None, FAKE, None, None, None, None, None]
-    assert lib.wsx_decode_step_workspace_bytes(4, 8192, 2048, 1024, 8, 157184) > (4 << 20)
+    assert lib.wsx_decode_step_workspace_bytes(4, 8192, 2048, 1024, 8, 157184) > (2 << 20)
     assert f(*args(st=big, T=4)) == 5
     assert f(*args(h=None)) == 1
     assert f(*args(T=6)) == 4

@@ -63,9 +63,12 @@ constexpr int kSpinMax = 1 << 17;  // polls before a wait gives up
 constexpr unsigned kEpochMod = (1u << 24) - 1;   // epochs cycle in [0, kEpochMod)
 // Copies of each exchange buffer: every consumer polls the copy picked by its
 // workgroup index, so no single cache line is hammered by hundreds of pollers.
-constexpr int kCopiesH = 8;        // residual stream
-constexpr int kCopiesLg = 16;      // router logits
-constexpr int kCopiesA = 8;        // expert activations
+// Each copy also costs its producer a store, so more copies is not better:
+// at the Ling shape 4 copies of the logits and of the activations beat 8 and
+// 16 (the residual stream's 8 are fixed by the down role's lane mapping).
+constexpr int kCopiesH = 8;        // residual stream (one copy per 8 lanes of the publishing wavefront)
+constexpr int kCopiesLg = 4;       // router logits
+constexpr int kCopiesA = 4;        // expert activations
 
 struct Ctl {   // control words, each on its own 256-byte line
   unsigned epoch;
